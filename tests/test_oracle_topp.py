@@ -1,0 +1,106 @@
+"""Pins for the float32 top-p selection procedure and its exponential."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import topp
+
+F = np.float32
+
+
+def test_exp32_accuracy_against_libm():
+    xs = np.concatenate([np.linspace(-87.0, 0.0, 20001), -np.logspace(-8, 1.9, 3000)]).astype(F)
+    got = topp.exp32(xs).astype(np.float64)
+    want = np.array([math.exp(float(x)) for x in xs])
+    rel = np.abs(got - want) / want
+    assert rel.max() < 4e-7          # a few float32 ulps
+
+
+def test_exp32_special_values():
+    assert topp.exp32(np.array([0.0], F))[0] == F(1.0)
+    assert topp.exp32(np.array([-88.0, -np.inf], F)).tolist() == [0.0, 0.0]
+    assert topp.exp32(np.array([-1.0], F))[0] == pytest.approx(math.exp(-1.0), rel=2e-7)
+
+
+def test_float32_cumsum_is_sequential():
+    rng = np.random.default_rng(1)
+    x = rng.random(3000).astype(F) * F(1e-3)
+    acc = F(0.0)
+    seq = []
+    for v in x:
+        acc = F(acc + v)
+        seq.append(acc)
+    assert np.array_equal(np.cumsum(x, dtype=F), np.array(seq, F))
+
+
+def test_tiny_p_keeps_exactly_the_top_min_blocks():
+    s = workloads.random_scores(2, 5, 300, seed=2)
+    keep = topp.topp_keep(s, 1e-30, 8)
+    for h in range(2):
+        for u in range(5):
+            want = np.argsort(-s[h, u].astype(np.float64), kind="stable")[:8]
+            assert set(np.flatnonzero(keep[h, u]).tolist()) == set(want.tolist())
+
+
+def test_kept_sets_nest_as_p_grows():
+    s = workloads.random_scores(1, 6, 200, seed=3)
+    prev = None
+    for p in (0.1, 0.3, 0.5, 0.7, 0.9, 0.99):
+        k = topp.topp_keep(s, p, 8)
+        if prev is not None:
+            assert np.all(k >= prev)
+        prev = k
+
+
+def test_equal_scores_keep_a_lowest_index_prefix():
+    s = np.zeros((1, 1, 50), F)
+    keep = topp.topp_keep(s, 0.5, 8)[0, 0]
+    k = int(keep.sum())
+    assert keep[:k].all() and not keep[k:].any()
+    assert k == 25           # 25 equal shares of 1/50 reach one half
+
+
+def test_one_dominant_score_keeps_min_blocks():
+    s = np.zeros((1, 1, 100), F)
+    s[0, 0, 37] = 50.0
+    keep = topp.topp_keep(s, 0.9, 8)[0, 0]
+    assert keep.sum() == 8 and keep[37] and keep[:7].all()
+
+
+def test_short_rows_keep_everything():
+    s = workloads.random_scores(1, 3, 5, seed=4)
+    assert topp.topp_keep(s, 0.5, 8).all()
+
+
+def test_agrees_with_float64_except_on_boundary_rows():
+    s = workloads.random_scores(2, 40, 400, seed=5, spread=2.0)
+    keep = topp.topp_keep(s, 0.9, 8)
+    disagree = 0
+    for h in range(2):
+        for u in range(40):
+            row = s[h, u].astype(np.float64)
+            order = np.argsort(-row, kind="stable")
+            c = np.cumsum(np.exp(row[order] - row.max()))
+            c /= c[-1]
+            k = max(int(np.argmax(c >= 0.9)) + 1, 8)
+            ref = np.zeros(400, bool)
+            ref[order[:k]] = True
+            if not np.array_equal(ref, keep[h, u]):
+                disagree += 1
+                assert topp.boundary_margin(row, 0.9, 8) < 1e-5
+    assert disagree <= 2
+
+
+def test_selection_mass_reaches_p():
+    s = workloads.random_scores(1, 20, 300, seed=6)
+    keep = topp.topp_keep(s, 0.9, 8)
+    for u in range(20):
+        row = s[0, u].astype(np.float64)
+        pr = np.exp(row - row.max()); pr /= pr.sum()
+        kept_mass = pr[keep[0, u]].sum()
+        assert kept_mass >= 0.9 - 1e-5
+        # dropping the smallest kept block falls below p (unless min-k binds)
+        if keep[0, u].sum() > 8:
+            assert kept_mass - pr[keep[0, u]].min() < 0.9 + 1e-5
