@@ -1,0 +1,175 @@
+"""Python entry points with the C ABI's names.
+
+Argument marshalling only: every function checks dtypes, shapes, devices and
+contiguity, allocates outputs with torch (device memory is the only thing torch
+provides here) and passes raw pointers plus torch's current HIP stream to the
+library.  All computation happens in the library's kernels.
+
+Masks travel as torch.int64 tensors holding the uint64 words bit for bit.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+import torch
+
+from ._lib import check, lib
+
+BLOCK = 64
+
+
+def mask_words(seq_len: int, block: int = BLOCK) -> int:
+    return int(lib().bsa_mask_words(int(seq_len), int(block)))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts):
+    d = ts[0].device
+    _need(d.type == "cuda", "tensors must live on a HIP device")
+    for t in ts:
+        _need(t.device == d, "all tensors must be on the same device")
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    return d
+
+
+def _check_mask(mask_bits, H, N):
+    nb = -(-N // BLOCK)
+    _need(mask_bits.dtype == torch.int64, "mask_bits must be int64 (uint64 words)")
+    _need(tuple(mask_bits.shape) == (H, nb, mask_words(N)),
+          f"mask_bits must be [{H}, {nb}, {mask_words(N)}], got {tuple(mask_bits.shape)}")
+
+
+def sparse_attn(q, k, v, mask_bits, scale=None, out=None, work_order=None):
+    """Block-sparse attention (sparse_attn_fwd / sparse_attn_fwd_f32 /
+    sparse_attn_fwd_planned).  q, k, v: [H, N, d] bf16 or fp32."""
+    _dev(q, k, v, mask_bits)
+    _need(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must share shape [H, N, d]")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    H, N, d = q.shape
+    _check_mask(mask_bits, H, N)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(q, out)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    s = _stream(q)
+    if q.dtype == torch.bfloat16:
+        if work_order is None:
+            rc = lib().sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits), H, N, d, BLOCK,
+                                       BLOCK, scale, _ptr(out), s)
+            check(rc, "sparse_attn_fwd")
+        else:
+            _dev(q, work_order)
+            _need(work_order.dtype == torch.int32 and work_order.numel() == H * (-(-N // BLOCK)),
+                  "work_order must be int32 [H * nb]")
+            rc = lib().sparse_attn_fwd_planned(_ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits),
+                                               _ptr(work_order), H, N, d, BLOCK, BLOCK, scale,
+                                               _ptr(out), s)
+            check(rc, "sparse_attn_fwd_planned")
+    elif q.dtype == torch.float32:
+        _need(work_order is None, "the fp32 path takes no work order")
+        rc = lib().sparse_attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits), H, N, d, BLOCK,
+                                       BLOCK, scale, _ptr(out), s)
+        check(rc, "sparse_attn_fwd_f32")
+    else:
+        raise ValueError("q, k, v must be bfloat16 or float32")
+    return out
+
+
+def plan(mask_bits, seq_len: int):
+    """Tile scheduler (sparse_attn_plan): returns (row_counts int32 [H*nb],
+    head_tiles int64 [H], work_order int32 [H*nb])."""
+    _dev(mask_bits)
+    H = mask_bits.shape[0]
+    _check_mask(mask_bits, H, seq_len)
+    nb = -(-seq_len // BLOCK)
+    counts = torch.empty(H * nb, dtype=torch.int32, device=mask_bits.device)
+    tiles = torch.empty(H, dtype=torch.int64, device=mask_bits.device)
+    order = torch.empty(H * nb, dtype=torch.int32, device=mask_bits.device)
+    rc = lib().sparse_attn_plan(_ptr(mask_bits), H, int(seq_len), BLOCK, _ptr(counts), _ptr(tiles),
+                                _ptr(order), _stream(mask_bits))
+    check(rc, "sparse_attn_plan")
+    return counts, tiles, order
+
+
+def mask_from_stripes(params, n_frames: int, frame_tokens: int, seq_len: int, out=None):
+    """PSA stripe tuples int32 [H, 7] (device) -> int64 mask words [H, nb, W]."""
+    _dev(params)
+    _need(params.dtype == torch.int32 and params.dim() == 2 and params.shape[1] == 7,
+          "params must be int32 [H, 7]")
+    H = params.shape[0]
+    nb = -(-seq_len // BLOCK)
+    if out is None:
+        out = torch.empty((H, nb, mask_words(seq_len)), dtype=torch.int64, device=params.device)
+    _check_mask(out, H, seq_len)
+    rc = lib().mask_from_stripes(_ptr(params), H, int(n_frames), int(frame_tokens), int(seq_len),
+                                 BLOCK, _ptr(out), _stream(params))
+    check(rc, "mask_from_stripes")
+    return out
+
+
+def block_scores_meanpool(q, k, scale=None, out=None):
+    """Mean-pooled block scores fp32 [H, nb, nb] from bf16 q, k [H, N, d]."""
+    _dev(q, k)
+    _need(q.dtype == k.dtype == torch.bfloat16 and q.shape == k.shape and q.dim() == 3,
+          "q, k must be bf16 [H, N, d]")
+    H, N, d = q.shape
+    nb = -(-N // BLOCK)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((H, nb, nb), dtype=torch.float32, device=q.device)
+    _need(out.shape == (H, nb, nb) and out.dtype == torch.float32, "out must be fp32 [H, nb, nb]")
+    rc = lib().block_scores_meanpool(_ptr(q), _ptr(k), H, N, d, BLOCK, scale, _ptr(out), _stream(q))
+    check(rc, "block_scores_meanpool")
+    return out
+
+
+def mask_from_block_scores_topp(scores, p: float, min_blocks: int, out=None):
+    """fp32 scores [H, nq, nk] -> int64 mask words [H, nq, ceil(nk/64)]."""
+    _dev(scores)
+    _need(scores.dtype == torch.float32 and scores.dim() == 3, "scores must be fp32 [H, nq, nk]")
+    H, nq, nk = scores.shape
+    if out is None:
+        out = torch.empty((H, nq, -(-nk // 64)), dtype=torch.int64, device=scores.device)
+    _need(out.shape == (H, nq, -(-nk // 64)) and out.dtype == torch.int64, "bad out")
+    rc = lib().mask_from_block_scores_topp(_ptr(scores), H, nq, nk, float(p), int(min_blocks),
+                                           _ptr(out), _stream(scores))
+    check(rc, "mask_from_block_scores_topp")
+    return out
+
+
+def permute_tokens(x, perm, inverse: bool = False, out=None):
+    """Gather (inverse=False) or scatter (inverse=True) token rows of x [H, N, d]."""
+    _dev(x, perm)
+    _need(x.dim() == 3 and perm.dtype == torch.int32 and perm.numel() == x.shape[1],
+          "x must be [H, N, d] and perm int32 [N]")
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(x, out)
+    H, N, d = x.shape
+    rc = lib().permute_tokens(_ptr(x), _ptr(perm), H, N, d, x.element_size(), int(bool(inverse)),
+                              _ptr(out), _stream(x))
+    check(rc, "permute_tokens")
+    return out
+
+
+def hilbert3d_order(T: int, H: int, W: int) -> np.ndarray:
+    """Host-only: int32 [T*H*W] token ids in 3D Hilbert order."""
+    perm = np.empty(T * H * W, dtype=np.int32)
+    rc = lib().hilbert3d_order(int(T), int(H), int(W), perm.ctypes.data_as(ctypes.c_void_p))
+    check(rc, "hilbert3d_order")
+    return perm

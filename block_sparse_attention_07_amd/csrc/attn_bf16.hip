@@ -1,0 +1,396 @@
+// Block-sparse attention forward, bf16 inputs, bf16 MFMA, fp32 online softmax.
+//
+// ScalingAttention, section 4.3.2 (CRM kernel) and Appendix E (Algorithm 2): a
+// FlashAttention forward whose dense key-block loop is replaced by a walk over
+// the set bits of the query block's packed row mask; kept 64x64 tiles are
+// computed densely, all other tiles are skipped without touching their K/V.
+//
+// gfx950 mapping (one workgroup of 4 waves per (head, query block)):
+//  * wave w owns query rows 32*(w&1) .. +31 and key half 32*(w>>1) .. +31 of every
+//    kept tile, so each wave keeps its own running max / sum and output
+//    accumulator; the two key halves are merged once at the end.
+//  * S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16 with K (A operand) from LDS and
+//    Q^T (B operand) held in registers for the whole row.  The accumulator gives
+//    lane l the logits of query row l%32 for 16 keys, so the row max and row sum
+//    are lane-local plus one exchange with lane l^32.
+//  * The same 16 probabilities, rounded to bf16, are exactly the B operand of
+//    O^T += V^T P^T, provided the A operand (V^T) pairs each k-slot with the key
+//    the accumulator register held.  V is therefore stored transposed in LDS with
+//    the key index's bits 2 and 3 swapped; every operand read is then one 16-byte
+//    LDS load.
+//  * Kept K/V tiles stream through a 2-stage LDS ring: the next tile's global
+//    loads are issued before the current tile's math and written to the other
+//    stage after it, with one barrier per tile.
+//  * The row's kept-block list is decoded once per 2048 blocks by wave 0: one mask
+//    word per lane, popcount, and a ballot-based exclusive prefix (one ballot per
+//    bit of the count) give every lane its write offset into an LDS list.
+//  * Softmax rescaling is lazy: the running max used for exponentials only moves
+//    when a tile's max exceeds it by more than 8 (a factor 256), which keeps every
+//    probability <= 256 and leaves the result exact up to rounding.
+#include <cmath>
+
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16;
+
+constexpr int BLK = 64;
+constexpr int NT = 256;
+constexpr int LIST_CAP = 2048;
+constexpr int CHUNK_WORDS = LIST_CAP / 64;
+constexpr int KPAD = 8;
+constexpr int VPAD = 8;
+constexpr float RESCALE_SLACK = 8.0f;
+
+template <int D>
+struct __attribute__((aligned(16))) Tiles {
+  u16 k[2][BLK][D + KPAD];    // K tile, row-major
+  u16 vt[2][D][BLK + VPAD];   // V tile, transposed, key bits 2 and 3 swapped
+};
+
+template <int D>
+struct __attribute__((aligned(16))) Merge {
+  float o[2][D / 2][64];      // [query-row half][accumulator register][lane]
+  float m[2][32];
+  float l[2][32];
+};
+
+template <int D>
+union __attribute__((aligned(16))) Smem {
+  Tiles<D> t;
+  Merge<D> mg;
+};
+
+__device__ __forceinline__ int swap_bits23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int n_heads, int N,
+    int nb, int W, float c, u16* __restrict__ O) {
+  constexpr int CPR = D / 8;             // 16-byte chunks per token row
+  constexpr int KCH = BLK * CPR / NT;    // K chunks per thread
+  constexpr int V_THREADS = 16 * CPR;    // threads that stage V (4 keys x 8 dims each)
+  constexpr int NDB = D / 32;            // 32-wide output column blocks
+  constexpr int NKS = D / 16;            // k-steps of the QK^T contraction
+
+  __shared__ Smem<D> sm;
+  __shared__ u16 list[LIST_CAP];
+  __shared__ int nlist;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rh = wave & 1;
+  const int kh = wave >> 1;
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+
+  int row_id = blockIdx.x;
+  if (order) {
+    row_id = order[blockIdx.x];
+    if (row_id < 0 || row_id >= n_heads * nb) return;
+  }
+  const int h = row_id / nb;
+  const int u = row_id - h * nb;
+  const size_t head_off = (size_t)h * N * D;
+  const u16* Qh = Q + head_off;
+  const u16* Kh = K + head_off;
+  const u16* Vh = V + head_off;
+  const uint64_t* mrow = mask + ((size_t)h * nb + u) * W;
+
+  // Q^T fragments (B operand): lane holds Q[row][16ks + 8g .. +7] of its query row.
+  bf16x8 qf[NKS];
+  {
+    // Rows past the sequence end read the last real row (always in bounds) and
+    // are zeroed by a select on the loaded value.
+    const int qrow = BLK * u + 32 * rh + r32;
+    const bool qvalid = qrow < N;
+    const int qsrc = qvalid ? qrow : N - 1;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 x = *reinterpret_cast<const uint4*>(Qh + (size_t)qsrc * D + 16 * ks + 8 * g);
+      if (!qvalid) x = make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+
+  // Staging registers for the next tile.
+  uint4 kreg[KCH];
+  uint4 vreg[4];
+  const int va = tid & 15;       // 4-key group of the V tile this thread stages
+  const int vc = tid >> 4;       // 8-dim chunk of the V tile this thread stages
+  const int vpos = swap_bits23(4 * va);
+
+  auto gload = [&](int vb) {
+    const int row0 = vb * BLK;
+    const uint4* Kt = reinterpret_cast<const uint4*>(Kh + (size_t)row0 * D);
+    const uint4* Vt = reinterpret_cast<const uint4*>(Vh + (size_t)row0 * D);
+    if (row0 + BLK <= N) {   // uniform: every row of the tile exists
+#pragma unroll
+      for (int r = 0; r < KCH; ++r) kreg[r] = Kt[tid + NT * r];
+      if (tid < V_THREADS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vreg[r] = Vt[(4 * va + r) * CPR + vc];
+      }
+    } else {                 // last, partial tile: clamp the row, zero the value
+      const int last = N - 1 - row0;
+#pragma unroll
+      for (int r = 0; r < KCH; ++r) {
+        const int ch = tid + NT * r;
+        const int kr = ch / CPR;
+        uint4 x = Kt[(kr <= last ? kr : last) * CPR + ch % CPR];
+        if (kr > last) x = make_uint4(0, 0, 0, 0);
+        kreg[r] = x;
+      }
+      if (tid < V_THREADS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 4 * va + r;
+          uint4 x = Vt[(key <= last ? key : last) * CPR + vc];
+          if (key > last) x = make_uint4(0, 0, 0, 0);
+          vreg[r] = x;
+        }
+      }
+    }
+  };
+
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int ch = tid + NT * r;
+      *reinterpret_cast<uint4*>(&sm.t.k[buf][ch / CPR][(ch % CPR) * 8]) = kreg[r];
+    }
+    if (tid < V_THREADS) {
+      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
+      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // dims 8*vc + 2*jj (low halves) and 8*vc + 2*jj + 1 (high halves) of keys 4va..4va+3
+        const uint2 lo = make_uint2((w0[jj] & 0xffffu) | (w1[jj] << 16), (w2[jj] & 0xffffu) | (w3[jj] << 16));
+        const uint2 hi = make_uint2((w0[jj] >> 16) | (w1[jj] & 0xffff0000u), (w2[jj] >> 16) | (w3[jj] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&sm.t.vt[buf][8 * vc + 2 * jj][vpos]) = lo;
+        *reinterpret_cast<uint2*>(&sm.t.vt[buf][8 * vc + 2 * jj + 1][vpos]) = hi;
+      }
+    }
+  };
+
+  auto compute = [&](int buf, int vb) {
+    const int key0 = vb * BLK + 32 * kh;
+    if (key0 >= N) return;   // this wave's key half lies entirely past the sequence end
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[buf][32 * kh + r32][16 * ks + 8 * g]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+    }
+    // s[i] is the logit of query row r32 for key 8*(i/4) + 4*g + i%4 of this half.
+    if (key0 + 32 > N) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + 8 * (i >> 2) + 4 * g + (i & 3) >= N) s[i] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * c;
+    if (__any(mt > m_run + RESCALE_SLACK)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_run = mn;
+    }
+    float p[16];
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
+      ls += p[i];
+    }
+    l_part += ls;
+    bf16x8 pb0, pb1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pb0[j] = (__bf16)p[j];
+      pb1[j] = (__bf16)p[8 + j];
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][32 * kh + 8 * g]);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, o[db], 0, 0, 0);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][32 * kh + 16 + 8 * g]);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, o[db], 0, 0, 0);
+    }
+  };
+
+  const int tail_bits = nb & 63;
+  const uint64_t lastmask = tail_bits ? ((1ull << tail_bits) - 1ull) : ~0ull;
+  const uint64_t lanes_below = (1ull << lane) - 1ull;
+
+  for (int w0 = 0; w0 < W; w0 += CHUNK_WORDS) {
+    __syncthreads();   // every wave is done with the previous chunk's list
+    if (wave == 0) {
+      const int wi = w0 + lane;
+      uint64_t word = 0;
+      if (lane < CHUNK_WORDS && wi < W) {
+        word = mrow[wi];
+        if (wi == W - 1) word &= lastmask;
+      }
+      const int cnt = __popcll(word);
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int b = 0; b < 7; ++b) {
+        const uint64_t bal = __ballot((cnt >> b) & 1);
+        pre += __popcll(bal & lanes_below) << b;
+        tot += __popcll(bal) << b;
+      }
+      const int base = 64 * wi;
+      while (word) {
+        list[pre++] = (u16)(base + __ffsll((unsigned long long)word) - 1);
+        word &= word - 1ull;
+      }
+      if (lane == 0) nlist = tot;
+    }
+    __syncthreads();
+    const int n = nlist;
+    if (n == 0) continue;
+    gload(list[0]);
+    sstore(0);
+    __syncthreads();
+    for (int t = 0; t < n; ++t) {
+      const int vb = list[t];
+      const bool more = t + 1 < n;
+      if (more) gload(list[t + 1]);
+      compute(t & 1, vb);
+      if (more) sstore((t + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // Merge the two key halves of each query-row half and write the output.
+  __syncthreads();
+  const float l_row = l_part + __shfl_xor(l_part, 32);
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.mg.o[rh][16 * db + i][lane] = o[db][i];
+    if (g == 0) {
+      sm.mg.m[rh][r32] = m_run;
+      sm.mg.l[rh][r32] = l_row;
+    }
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = sm.mg.m[rh][r32];
+    const float l1 = sm.mg.l[rh][r32];
+    const float mm = fmaxf(m_run, m1);
+    float a0 = 0.f, a1 = 0.f;
+    if (mm != -INFINITY) {
+      a0 = __builtin_amdgcn_exp2f(m_run - mm);
+      a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    }
+    const float L = l_row * a0 + l1 * a1;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    const int row = BLK * u + 32 * rh + r32;
+    if (row < N) {
+      u16* orow = O + head_off + (size_t)row * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 y;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * q4 + r;
+            y[r] = (__bf16)((o[db][i] * a0 + sm.mg.o[rh][16 * db + i][lane] * a1) * inv);
+          }
+          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * q4 + 4 * g) = y;
+        }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_attn_bf16(const void* q, const void* k, const void* v, const uint64_t* mask,
+                     const int32_t* order, int n_heads, int seq_len, int head_dim, float scale,
+                     void* out, hipStream_t stream) {
+  const int nb = n_blocks(seq_len, 64);
+  const int W = n_words(nb);
+  if (nb > 65535) return fail(BSA_ERR_UNSUPPORTED, "at most 65535 key blocks per head (seq_len %d)", seq_len);
+  const float c = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)(n_heads * nb)), block(NT);
+  const u16* Q = static_cast<const u16*>(q);
+  const u16* K = static_cast<const u16*>(k);
+  const u16* V = static_cast<const u16*>(v);
+  u16* O = static_cast<u16*>(out);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, block, 0, stream, Q, K, V, mask, order,
+                       n_heads, seq_len, nb, W, c, O);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, block, 0, stream, Q, K, V, mask, order,
+                       n_heads, seq_len, nb, W, c, O);
+  BSA_CHECK_HIP(hipGetLastError());
+  return ok();
+}
+
+}  // namespace bsa
+
+extern "C" int sparse_attn_fwd(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                               int n_heads, int seq_len, int head_dim, int block_q, int block_k,
+                               float scale, void* out, hipStream_t stream) {
+  using namespace bsa;
+  int rc = check_attn_args(q, k, v, mask_bits, out, n_heads, seq_len, head_dim, block_q, block_k,
+                           scale, 16);
+  if (rc) return rc;
+  const size_t rows = (size_t)n_heads * n_blocks(seq_len, 64);
+  const size_t off_tiles = (rows * 4 + 255) & ~size_t(255);
+  const size_t off_order = (off_tiles + (size_t)n_heads * 8 + 255) & ~size_t(255);
+  char* ws = static_cast<char*>(scratch(off_order + rows * 4, stream));
+  if (!ws) return BSA_ERR_HIP;
+  int32_t* counts = reinterpret_cast<int32_t*>(ws);
+  int64_t* tiles = reinterpret_cast<int64_t*>(ws + off_tiles);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + off_order);
+  rc = launch_plan(mask_bits, n_heads, seq_len, counts, tiles, order, stream);
+  if (rc) return rc;
+  return launch_attn_bf16(q, k, v, mask_bits, order, n_heads, seq_len, head_dim, scale, out, stream);
+}
+
+extern "C" int sparse_attn_fwd_planned(const void* q, const void* k, const void* v,
+                                       const uint64_t* mask_bits, const int32_t* work_order,
+                                       int n_heads, int seq_len, int head_dim, int block_q,
+                                       int block_k, float scale, void* out, hipStream_t stream) {
+  using namespace bsa;
+  int rc = check_attn_args(q, k, v, mask_bits, out, n_heads, seq_len, head_dim, block_q, block_k,
+                           scale, 16);
+  if (rc) return rc;
+  if (!work_order || !aligned(work_order, 4))
+    return fail(BSA_ERR_INVALID_ARG, "work_order must be a non-null 4-byte aligned pointer");
+  return launch_attn_bf16(q, k, v, mask_bits, work_order, n_heads, seq_len, head_dim, scale, out,
+                          stream);
+}

@@ -1,0 +1,49 @@
+// Internal helpers shared by the library's translation units: error state,
+// argument checks, per-device scratch memory and small device utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/bsattn.h"
+
+namespace bsa {
+
+// Record a message for bsa_last_error() and return `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the thread's message; returns BSA_OK.
+int ok();
+// Map a HIP status to BSA_ERR_HIP with the call site named.
+int hip_fail(hipError_t e, const char* what);
+
+// Per-device scratch buffer owned by the library, grown on demand.  Returns
+// nullptr (with the error recorded) when allocation fails.
+void* scratch(size_t bytes, hipStream_t stream);
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int n_blocks(int seq_len, int block) { return (seq_len + block - 1) / block; }
+inline int n_words(int nb) { return (nb + 63) / 64; }
+
+// Checks shared by the attention entry points.
+int check_attn_args(const void* q, const void* k, const void* v, const void* mask, const void* out,
+                    int n_heads, int seq_len, int head_dim, int block_q, int block_k, float scale,
+                    size_t elem_align);
+
+// Launch the row-count / head-order planner (defined in plan.hip).
+int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts, int64_t* head_tiles,
+                int32_t* order, hipStream_t stream);
+
+// Launch the bf16 attention kernel with an optional work order (attn_bf16.hip).
+int launch_attn_bf16(const void* q, const void* k, const void* v, const uint64_t* mask,
+                     const int32_t* order, int n_heads, int seq_len, int head_dim, float scale,
+                     void* out, hipStream_t stream);
+
+}  // namespace bsa
+
+#define BSA_CHECK_HIP(call)                                  \
+  do {                                                       \
+    hipError_t _e = (call);                                  \
+    if (_e != hipSuccess) return ::bsa::hip_fail(_e, #call); \
+  } while (0)

@@ -1,0 +1,92 @@
+// Tile scheduler: per-row kept-block counts, per-head totals and a work order.
+//
+// The packed row mask (ScalingAttention, section 4.3.2) already tells how many
+// kept tiles each (head, query block) row will run; a popcount pass turns that
+// into a schedule.  Heads run in decreasing total work so the heaviest heads are
+// dispatched first and the lightest fill the tail; within a head, query blocks
+// stay in order so that concurrently resident workgroups of one head share
+// that head's K/V in the caches.
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+__global__ void fill_i64_kernel(int64_t* __restrict__ p, int n, int64_t value) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+__global__ void row_counts_kernel(const uint64_t* __restrict__ mask, int n_rows, int nb, int W,
+                                  uint64_t lastmask, int32_t* __restrict__ counts,
+                                  int64_t* __restrict__ head_tiles) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n_rows) return;
+  const uint64_t* m = mask + (size_t)row * W;
+  int c = 0;
+  for (int w = 0; w < W - 1; ++w) c += __popcll(m[w]);
+  c += __popcll(m[W - 1] & lastmask);
+  counts[row] = c;
+  atomicAdd(reinterpret_cast<unsigned long long*>(head_tiles + row / nb), (unsigned long long)c);
+}
+
+// One workgroup per head: rank the head among all heads (more work first, ties
+// by head index) and write its rows at that rank's slot of the order.
+__global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restrict__ head_tiles,
+                                                         int n_heads, int nb,
+                                                         int32_t* __restrict__ order) {
+  __shared__ int partial[256];
+  const int h = blockIdx.x;
+  const int64_t mine = head_tiles[h];
+  int before = 0;
+  for (int j = threadIdx.x; j < n_heads; j += blockDim.x) {
+    const int64_t t = head_tiles[j];
+    before += (t > mine) || (t == mine && j < h);
+  }
+  partial[threadIdx.x] = before;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) partial[threadIdx.x] += partial[threadIdx.x + s];
+    __syncthreads();
+  }
+  const int rank = partial[0];
+  for (int u = threadIdx.x; u < nb; u += blockDim.x) order[(size_t)rank * nb + u] = h * nb + u;
+}
+
+}  // namespace
+
+int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts, int64_t* head_tiles,
+                int32_t* order, hipStream_t stream) {
+  const int nb = n_blocks(seq_len, 64);
+  const int W = n_words(nb);
+  const int rows = n_heads * nb;
+  const int tail = nb & 63;
+  const uint64_t lastmask = tail ? ((1ull << tail) - 1ull) : ~0ull;
+  hipLaunchKernelGGL(fill_i64_kernel, dim3((n_heads + 255) / 256), dim3(256), 0, stream, head_tiles,
+                     n_heads, (int64_t)0);
+  BSA_CHECK_HIP(hipGetLastError());
+  hipLaunchKernelGGL(row_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, mask, rows,
+                     nb, W, lastmask, counts, head_tiles);
+  BSA_CHECK_HIP(hipGetLastError());
+  hipLaunchKernelGGL(head_order_kernel, dim3(n_heads), dim3(256), 0, stream, head_tiles, n_heads,
+                     nb, order);
+  BSA_CHECK_HIP(hipGetLastError());
+  return ok();
+}
+
+}  // namespace bsa
+
+extern "C" int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int block,
+                                int32_t* row_counts, int64_t* head_tiles, int32_t* work_order,
+                                hipStream_t stream) {
+  using namespace bsa;
+  if (!mask_bits || !row_counts || !head_tiles || !work_order)
+    return fail(BSA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(mask_bits, 8) || !aligned(head_tiles, 8) || !aligned(row_counts, 4) ||
+      !aligned(work_order, 4))
+    return fail(BSA_ERR_INVALID_ARG, "misaligned pointer argument");
+  if (n_heads < 1 || seq_len < 1) return fail(BSA_ERR_INVALID_ARG, "n_heads and seq_len must be >= 1");
+  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "only 64-token blocks are implemented");
+  if ((long long)n_heads * n_blocks(seq_len, 64) > 0x7fffffffLL)
+    return fail(BSA_ERR_INVALID_ARG, "problem too large");
+  return launch_plan(mask_bits, n_heads, seq_len, row_counts, head_tiles, work_order, stream);
+}

@@ -1,0 +1,200 @@
+/*
+ * bsattn.h -- block-sparse video-DiT self-attention for AMD MI355X (gfx950).
+ *
+ * One operation and its mask producers, exported with a plain C ABI:
+ *
+ *   O = softmax(scale * Q K^T + M) V,   M = 0 on kept 64x64 blocks, -inf elsewhere,
+ *
+ * over the flattened (frame, height, width) tokens of one video-DiT attention
+ * layer.  This is the bit-wise block-sparse FlashAttention kernel of
+ * ScalingAttention (section 4.3.2, "CRM kernel"; Appendix E, Algorithm 2), the
+ * same operation PSA runs under stripe masks (PSA page, Figure 3) and that online
+ * top-p methods run under predicted block masks (SCOPE and "Competition Domains
+ * Matter" abstracts).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers owned by the caller unless marked "host".  The
+ *   library never frees or retains them.
+ * - Tensors are dense and row-major:  q, k, v, out are [n_heads][seq_len][head_dim]
+ *   (batch folded into n_heads).  bf16 entry points take raw bfloat16 storage.
+ * - Mask rows (the packed row mask, "CRM" in ScalingAttention section 4.3.2) are
+ *   uint64 [n_heads][nb][W] with nb = ceil(seq_len / 64) and W = ceil(nb / 64);
+ *   bit b (least significant = 0) of word w marks key block 64*w + b as kept for
+ *   that query block.  Bits at positions >= nb are ignored.
+ * - seq_len is the real token count; keys at positions >= seq_len in the last
+ *   block do not exist (they are excluded, never treated as zero keys).
+ *   A query row whose mask row keeps no block produces an output of 0.
+ * - Every device entry point is stream-ordered and asynchronous: it validates its
+ *   arguments on the host, enqueues kernels on `stream` and returns.  Faults of
+ *   enqueued kernels surface at the caller's next synchronisation.
+ * - Return value: BSA_OK (0) or an error code; a thread-local message describing
+ *   the last error is available from bsa_last_error().  Argument errors are
+ *   detected before any HIP call, so nothing is enqueued when one is returned.
+ *   The library never aborts and never throws across this boundary.
+ * - Alignment: q, k, v, out, scores and x/y must be 16-byte aligned; mask and
+ *   index arrays 8- and 4-byte aligned respectively.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_OK 0
+#define BSA_ERR_INVALID_ARG 1   /* null/misaligned pointer, bad size, non-finite scale ... */
+#define BSA_ERR_UNSUPPORTED 2   /* valid but not implemented (block != 64, head_dim not 64/128) */
+#define BSA_ERR_HIP 3           /* a HIP runtime call failed; message holds hipGetErrorString */
+
+/* Message for the last error returned on this host thread ("" if none). */
+const char* bsa_last_error(void);
+
+/* Words per mask row, ceil(ceil(seq_len / block) / 64); -1 if seq_len < 1 or block < 1.
+ * ScalingAttention section 4.3.2: one word load decodes as many blocks as the word
+ * has bits (the pages' 32-bit words and 128-token blocks give 64 loads per row at
+ * 256k tokens; this library's 64-bit words and 64-token blocks give 31 at 126,720). */
+int bsa_mask_words(int seq_len, int block);
+
+/*
+ * sparse_attn_fwd -- block-sparse attention forward, bfloat16 in/out, fp32 softmax.
+ * ScalingAttention section 4.3.2 and Appendix E (Algorithm 2): each (head, query
+ * block) workgroup walks the set bits of its mask row and runs dense FlashAttention
+ * tiles only on kept key blocks, with an online softmax (running max and sum).
+ *
+ *   q, k, v    bf16 [n_heads][seq_len][head_dim], read only.
+ *   mask_bits  uint64 [n_heads][nb][W] as above, read only.
+ *   n_heads    >= 1;  seq_len >= 1;  head_dim in {64, 128};
+ *   block_q, block_k  must both be 64 (else BSA_ERR_UNSUPPORTED);
+ *   scale      finite and > 0 (typically 1/sqrt(head_dim));
+ *   out        bf16 [n_heads][seq_len][head_dim], written (round to nearest even).
+ *
+ * Work is ordered by a device-side planning pass (row popcounts, heads in
+ * decreasing kept-block count) kept in a library-owned per-device scratch buffer
+ * that grows on demand; calls that overlap on one device from different streams
+ * race on that buffer -- use sparse_attn_plan + sparse_attn_fwd_planned with
+ * caller-owned buffers for concurrent use.
+ */
+int sparse_attn_fwd(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                    int n_heads, int seq_len, int head_dim, int block_q, int block_k,
+                    float scale, void* out, hipStream_t stream);
+
+/*
+ * sparse_attn_fwd_f32 -- same operation and arguments with fp32 q, k, v, out and
+ * fp32 arithmetic throughout (reference-precision path for small cases).
+ */
+int sparse_attn_fwd_f32(const float* q, const float* k, const float* v, const uint64_t* mask_bits,
+                        int n_heads, int seq_len, int head_dim, int block_q, int block_k,
+                        float scale, float* out, hipStream_t stream);
+
+/*
+ * sparse_attn_plan -- the tile scheduler on its own.  For static masks (computed
+ * offline and reused across denoising steps, ScalingAttention section 4.1 and
+ * Appendix A) the plan can be computed once and reused.
+ *
+ *   mask_bits   uint64 [n_heads][nb][W], read only.
+ *   row_counts  int32 [n_heads * nb], written: kept blocks of each (head, query block) row.
+ *   head_tiles  int64 [n_heads], written: kept blocks of each head.
+ *   work_order  int32 [n_heads * nb], written: a permutation of row ids (h * nb + u):
+ *               heads in decreasing head_tiles (ties by head index), rows of one head
+ *               in increasing u.
+ */
+int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int block,
+                     int32_t* row_counts, int64_t* head_tiles, int32_t* work_order,
+                     hipStream_t stream);
+
+/*
+ * sparse_attn_fwd_planned -- sparse_attn_fwd with a caller-provided work order
+ * (any permutation of [0, n_heads * nb), normally from sparse_attn_plan).  Uses no
+ * library scratch memory.  Entries outside [0, n_heads * nb) are skipped.
+ */
+int sparse_attn_fwd_planned(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                            const int32_t* work_order, int n_heads, int seq_len, int head_dim,
+                            int block_q, int block_k, float scale, void* out, hipStream_t stream);
+
+/*
+ * mask_from_stripes -- expand per-head PSA stripe tuples into packed row masks.
+ * PSA page, Figure 3 and Appendix Tables 7-9: per head either "full window" or a
+ * temporal (width, offset, stride) and a spatial (width, offset, stride) stripe.
+ * Reading used (the page names the parameters but prints no predicate): distances
+ * are key minus query, in frames (temporal) and in 64-token spatial blocks of the
+ * frame (spatial); x = dist - offset + width/2 (integer division); a stride of 0
+ * means a single band, 0 <= x < width; otherwise the stride is the gap between
+ * stripes and the band repeats with period width + stride, (x mod period) < width.
+ * A pair is kept when full, or when both the temporal and spatial tests hold.
+ * When frame_tokens is not a multiple of block, a block is placed by its first token.
+ *
+ *   params      int32 [n_heads][7] = {full, Tw, To, Ts, Sw, So, Ss}; widths >= 1,
+ *               strides >= 0 (device memory).
+ *   n_frames, frame_tokens  with n_frames * frame_tokens == seq_len.
+ *   block       must be 64.
+ *   mask_bits   uint64 [n_heads][nb][W], written in full (padding bits zero).
+ * Widths/strides are not checked on the device; a width < 1 keeps nothing.
+ */
+int mask_from_stripes(const int32_t* params, int n_heads, int n_frames, int frame_tokens,
+                      int seq_len, int block, uint64_t* mask_bits, hipStream_t stream);
+
+/*
+ * block_scores_meanpool -- block proxy scores for online mask prediction (SCOPE
+ * abstract: masks predicted from block-level proxy scores; pooling as in
+ * ScalingAttention Eq. 1).  qbar_u, kbar_v are fp32 means over the real tokens of
+ * each 64-token block; scores[h][u][v] = scale * <qbar_u, kbar_v> in fp32.
+ *
+ *   q, k     bf16 [n_heads][seq_len][head_dim], head_dim in {64, 128}; block must be 64.
+ *   scores   fp32 [n_heads][nb][nb], written.
+ * Uses the library's per-device scratch buffer for the pooled means (see
+ * sparse_attn_fwd about overlapping calls).
+ */
+int block_scores_meanpool(const void* q, const void* k, int n_heads, int seq_len, int head_dim,
+                          int block, float scale, float* scores, hipStream_t stream);
+
+/*
+ * mask_from_block_scores_topp -- hybrid top-p selection with a top-k minimum
+ * ("Competition Domains Matter" and SCOPE abstracts; cumulative-mass cut-off as in
+ * ScalingAttention Appendix A, Algorithm 1).  Per row of n = n_k_blocks scores, in
+ * float32 with every operation rounded to nearest and never fused:
+ *   m = max s;  e_j = EXP(s_j - m)  (the library's Cody-Waite + degree-7 Taylor exp,
+ *   0 below -87);  order = s descending, ties to the lower index;  Z = sequential sum
+ *   of e in that order;  c accumulates e/Z in that order and the first position where
+ *   c >= p gives k_p (k_p = n if never);  keep the first max(k_p, min(min_blocks, n))
+ *   blocks of the order.
+ *
+ *   scores      fp32 [n_heads][n_q_blocks][n_k_blocks], finite; 1 <= n_k_blocks <= 4096.
+ *   p           in (0, 1];  min_blocks >= 0.
+ *   mask_bits   uint64 [n_heads][n_q_blocks][ceil(n_k_blocks/64)], written in full.
+ */
+int mask_from_block_scores_topp(const float* scores, int n_heads, int n_q_blocks, int n_k_blocks,
+                                float p, int min_blocks, uint64_t* mask_bits, hipStream_t stream);
+
+/*
+ * permute_tokens -- token reordering for Hilbert-ordered attention (DFSAttn
+ * abstract: tokens reordered along a Hilbert curve before block-sparse attention;
+ * SCOPE abstract: attention is then taken over the selected original keys/values,
+ * so the output is scattered back).
+ *   inverse = 0:  y[h][i][:] = x[h][perm[i]][:]      (gather into curve order)
+ *   inverse = 1:  y[h][perm[i]][:] = x[h][i][:]      (scatter back)
+ *   x, y        [n_heads][seq_len][head_dim] of elem_bytes each (2 or 4); x != y.
+ *   perm        int32 [seq_len], a permutation of [0, seq_len); out-of-range
+ *               entries are skipped (their rows of y are left untouched).
+ *   head_dim * elem_bytes must be a multiple of 16.
+ */
+int permute_tokens(const void* x, const int32_t* perm, int n_heads, int seq_len, int head_dim,
+                   int elem_bytes, int inverse, void* y, hipStream_t stream);
+
+/*
+ * hilbert3d_order -- host-only, synchronous.  perm_host (int32 [T*H*W], host memory)
+ * receives the token ids (t-major id t*H*W + y*W + x) in increasing 3D Hilbert index,
+ * using J. Skilling's transpose construction ("Programming the Hilbert curve", 2004)
+ * on the smallest 2^b cube holding the grid, axes ordered (t, y, x).
+ * T, H, W >= 1 and T*H*W < 2^31.
+ */
+int hilbert3d_order(int T, int H, int W, int32_t* perm_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

@@ -1,0 +1,136 @@
+"""GPU parity of the mask producers and the token permutation: bit-exact where
+the result is an integer (stripes, top-p, permutation), within a derived
+tolerance for the float block scores; plus the full dynamic top-p pipeline."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_07_amd as bsa
+import workloads
+from oracle import block_scores, crm, hilbert, stripes, topp
+from oracle.attention import sparse_attention
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+B = 64
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _stripe_case(params, T, F):
+    params = np.asarray(params, np.int32)
+    m = bsa.mask_from_stripes(gu.to_dev(params), T, F, T * F)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.mask_host(m), stripes.stripe_mask_bits(params, T, F, T * F))
+
+
+def test_stripes_printed_tuples_bit_exact():
+    g = json.load(open(os.path.join(GOLD, "psa_stripe_tuples.json")))
+    rows = [[1, 1, 0, 0, 1, 0, 0]] + [[0] + t for tab in g["tables"].values() for t in tab]
+    _stripe_case(rows, 33, 60 * 64)          # HunyuanVideo 768x1280 latent grid
+    _stripe_case(rows, 21, 3600)             # Wan 720p: 3600-token frames (not whole blocks)
+
+
+def test_stripes_random_tuples_and_odd_frames():
+    rng = np.random.default_rng(21)
+    params = np.zeros((20, 7), np.int32)
+    for i in range(20):
+        params[i] = (int(rng.random() < 0.1), rng.integers(1, 12), rng.integers(-3, 4), rng.integers(0, 5),
+                     rng.integers(1, 11), rng.integers(-2, 3), rng.integers(0, 7))
+    for T, F in [(5, 64 * 7), (7, 100), (3, 1560), (1, 130)]:
+        _stripe_case(params, T, F)
+
+
+@pytest.mark.parametrize("nk", [1, 5, 64, 65, 1182, 2048, 4096])
+def test_topp_bit_exact_random_scores(nk):
+    s = workloads.random_scores(3, 17, nk, seed=nk)
+    s[0, 0] = 0.0                                   # all ties
+    s[0, 1] = np.round(s[0, 1])                     # many ties
+    s[1, 2, nk // 2] = 40.0                         # one dominant block
+    sd = gu.to_dev(s)
+    for p, mb in [(0.9, 8), (0.5, 0), (0.99, 3), (1.0, 8), (1e-6, 8)]:
+        m = bsa.mask_from_block_scores_topp(sd, p, mb)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.mask_host(m), topp.topp_mask_bits(s, p, mb)), (p, mb)
+
+
+def test_block_scores_within_fp32_bound():
+    n, d = 64 * 37 + 9, 128
+    rng = np.random.default_rng(22)
+    q = workloads.bf16_bits(rng.standard_normal((3, n, d)).astype(np.float32))
+    k = workloads.bf16_bits(rng.standard_normal((3, n, d)).astype(np.float32))
+    scale = 1.0 / np.sqrt(d)
+    got = bsa.block_scores_meanpool(gu.to_dev(q, True), gu.to_dev(k, True), scale)
+    torch.cuda.synchronize()
+    qf, kf = workloads.bf16_to_f32(q).astype(np.float64), workloads.bf16_to_f32(k).astype(np.float64)
+    ref = block_scores.block_scores(qf, kf, scale)
+    # fp32 error bound: means carry <= 64 eps relative error, the dot product
+    # <= d eps of sum |qbar||kbar| -- bounded by 4e-5 * scale * sum|qbar_c kbar_c|
+    qb, kb = block_scores.block_means(qf), block_scores.block_means(kf)
+    bound = 4e-5 * scale * np.einsum("hud,hvd->huv", np.abs(qb), np.abs(kb)) + 1e-12
+    err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+def test_permute_gather_scatter_exact():
+    rng = np.random.default_rng(23)
+    n, d = 1000, 128
+    x = workloads.bf16_bits(rng.standard_normal((2, n, d)).astype(np.float32))
+    perm = rng.permutation(n).astype(np.int32)
+    xd, pd = gu.to_dev(x, True), gu.to_dev(perm)
+    y = bsa.permute_tokens(xd, pd)
+    z = bsa.permute_tokens(y, pd, inverse=True)
+    torch.cuda.synchronize()
+    yh = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(yh, hilbert.permute_rows(x, perm))
+    assert np.array_equal(z.cpu().view(torch.int16).numpy().view(np.uint16), x)
+    xf = rng.standard_normal((1, n, 64)).astype(np.float32)
+    yf = bsa.permute_tokens(gu.to_dev(xf), pd, inverse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(yf.cpu().numpy(), hilbert.permute_rows(xf, perm, inverse=True))
+
+
+def test_topp_pipeline_end_to_end():
+    """Hilbert permute -> block scores -> top-p mask -> attention -> unpermute, at
+    the Wan2.1-14B 720p shape, against the oracle pipeline."""
+    w = workloads.WORKLOADS["topp_wan14b"]
+    T, Hh, Ww = w.grid
+    p, mb = 0.9, 8
+    perm = bsa.hilbert3d_order(T, Hh, Ww)
+    assert np.array_equal(perm, hilbert.hilbert_order(T, Hh, Ww))
+    q, k, v = workloads.qkv(w)
+    pd = gu.to_dev(perm)
+    qd, kd, vd = (bsa.permute_tokens(gu.to_dev(x, True), pd) for x in (q, k, v))
+    sc = bsa.block_scores_meanpool(qd, kd, w.scale)
+    mask = bsa.mask_from_block_scores_topp(sc, p, mb)
+    yd = bsa.sparse_attn(qd, kd, vd, mask, w.scale)
+    out = bsa.permute_tokens(yd, pd, inverse=True)
+    torch.cuda.synchronize()
+    bits_gpu = gu.mask_host(mask)
+    # oracle pipeline: float64 scores, rounded once to float32, then the float32 selection
+    qp = hilbert.permute_rows(q, perm)
+    kp = hilbert.permute_rows(k, perm)
+    vp = hilbert.permute_rows(v, perm)
+    f = lambda x: workloads.bf16_to_f32(x).astype(np.float64)
+    s_ref = np.stack([block_scores.block_scores(f(qp[h:h + 1]), f(kp[h:h + 1]), w.scale)[0]
+                      for h in range(w.n_heads)])
+    bits_ref = topp.topp_mask_bits(s_ref.astype(np.float32), p, mb)
+    same = np.all(bits_gpu == bits_ref, axis=-1)
+    print(f"[topp] density {crm.unpack_rows(bits_gpu, w.n_blocks).mean():.4f}, "
+          f"rows differing {int((~same).sum())} of {same.size}", flush=True)
+    assert (~same).sum() <= max(5, same.size // 1000)
+    for h, u in zip(*np.nonzero(~same)):
+        assert topp.boundary_margin(s_ref[h, u], p, mb) < 1e-4
+    keep = crm.unpack_rows(bits_ref, w.n_blocks)
+    blocks = [b for b in gu.sample_blocks(keep, 16, seed=w.seed) if same[b]]
+    hs = sorted({h for h, _ in blocks})
+    hmap = {h: i for i, h in enumerate(hs)}
+    qf, kf, vf = (np.stack([f(x[h]) for h in hs]) for x in (qp, kp, vp))
+    ref = sparse_attention(qf, kf, vf, bits_ref[hs], w.scale, blocks=[(hmap[h], u) for h, u in blocks])
+    outh = out.cpu()
+    for (h, u), r in zip(blocks, ref):
+        rows = perm[u * B:u * B + r.shape[0]]
+        g = gu.bf16_host(outh[h][torch.from_numpy(rows.astype(np.int64))])
+        gu.assert_bf16_close(g, r, f"topp ({h},{u})")
