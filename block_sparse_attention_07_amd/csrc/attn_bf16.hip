@@ -38,6 +38,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BLK = 64;
 constexpr int NT = 256;
@@ -46,6 +48,9 @@ constexpr int CHUNK_WORDS = LIST_CAP / 64;
 constexpr int KPAD = 8;
 constexpr int VPAD = 8;
 constexpr float RESCALE_SLACK = 8.0f;
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family GPUs:
+// 32-bit data format, so the per-access range check against num_records applies.
+constexpr int BUFFER_DWORD3 = 0x00020000;
 
 template <int D>
 struct __attribute__((aligned(16))) Tiles {
@@ -130,42 +135,43 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  // Staging registers for the next tile.
-  uint4 kreg[KCH];
-  uint4 vreg[4];
+  // Staging registers for the next tile (vector values, so they stay in VGPRs):
+  // K chunk r of this thread in dwords 4r..4r+3 of kreg, V key 4va+r in vreg.
+  static_assert(KCH <= 4, "K staging holds at most four 16-byte chunks");
+  u32x16 kreg = {};
+  u32x16 vreg = {};
   const int va = tid & 15;       // 4-key group of the V tile this thread stages
   const int vc = tid >> 4;       // 8-dim chunk of the V tile this thread stages
   const int vpos = swap_bits23(4 * va);
+  constexpr bool ALL_STAGE_V = V_THREADS == NT;
+
+  // Tiles are read with raw buffer loads: one descriptor per head, a scalar
+  // byte offset for the tile and per-thread byte offsets fixed for the whole
+  // row.  The descriptor's range check returns zeros for rows at or past the
+  // sequence end (the ragged last block), which are masked out of the softmax.
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)head_bytes, BUFFER_DWORD3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Vh), 0, (int)head_bytes, BUFFER_DWORD3);
+  u32x4 koff = {}, voff = {};
+#pragma unroll
+  for (int r = 0; r < KCH; ++r) koff[r] = (uint32_t)((tid + NT * r) * 16);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) voff[r] = (uint32_t)(((4 * va + r) * CPR + vc) * 16);
 
   auto gload = [&](int vb) {
-    const int row0 = vb * BLK;
-    const uint4* Kt = reinterpret_cast<const uint4*>(Kh + (size_t)row0 * D);
-    const uint4* Vt = reinterpret_cast<const uint4*>(Vh + (size_t)row0 * D);
-    if (row0 + BLK <= N) {   // uniform: every row of the tile exists
+    const int tile_off = vb * BLK * D * 2;
 #pragma unroll
-      for (int r = 0; r < KCH; ++r) kreg[r] = Kt[tid + NT * r];
-      if (tid < V_THREADS) {
+    for (int r = 0; r < KCH; ++r) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)koff[r], tile_off, 0);
+      kreg[4 * r] = x[0]; kreg[4 * r + 1] = x[1]; kreg[4 * r + 2] = x[2]; kreg[4 * r + 3] = x[3];
+    }
+    if (ALL_STAGE_V || tid < V_THREADS) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[r] = Vt[(4 * va + r) * CPR + vc];
-      }
-    } else {                 // last, partial tile: clamp the row, zero the value
-      const int last = N - 1 - row0;
-#pragma unroll
-      for (int r = 0; r < KCH; ++r) {
-        const int ch = tid + NT * r;
-        const int kr = ch / CPR;
-        uint4 x = Kt[(kr <= last ? kr : last) * CPR + ch % CPR];
-        if (kr > last) x = make_uint4(0, 0, 0, 0);
-        kreg[r] = x;
-      }
-      if (tid < V_THREADS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 4 * va + r;
-          uint4 x = Vt[(key <= last ? key : last) * CPR + vc];
-          if (key > last) x = make_uint4(0, 0, 0, 0);
-          vreg[r] = x;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)voff[r], tile_off, 0);
+        vreg[4 * r] = x[0]; vreg[4 * r + 1] = x[1]; vreg[4 * r + 2] = x[2]; vreg[4 * r + 3] = x[3];
       }
     }
   };
@@ -174,18 +180,19 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
       const int ch = tid + NT * r;
-      *reinterpret_cast<uint4*>(&sm.t.k[buf][ch / CPR][(ch % CPR) * 8]) = kreg[r];
+      *reinterpret_cast<uint4*>(&sm.t.k[buf][ch / CPR][(ch % CPR) * 8]) =
+          make_uint4(kreg[4 * r], kreg[4 * r + 1], kreg[4 * r + 2], kreg[4 * r + 3]);
     }
-    if (tid < V_THREADS) {
-      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+    if (ALL_STAGE_V || tid < V_THREADS) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        // dims 8*vc + 2*jj (low halves) and 8*vc + 2*jj + 1 (high halves) of keys 4va..4va+3
-        const uint2 lo = make_uint2((w0[jj] & 0xffffu) | (w1[jj] << 16), (w2[jj] & 0xffffu) | (w3[jj] << 16));
-        const uint2 hi = make_uint2((w0[jj] >> 16) | (w1[jj] & 0xffff0000u), (w2[jj] >> 16) | (w3[jj] & 0xffff0000u));
+        // dims 8*vc + 2*jj (low halves) and 8*vc + 2*jj + 1 (high halves) of
+        // keys 4va..4va+3, packed two keys per dword with one byte permute each
+        const uint32_t w0 = vreg[jj], w1 = vreg[4 + jj], w2 = vreg[8 + jj], w3 = vreg[12 + jj];
+        const uint2 lo = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x05040100u),
+                                    __builtin_amdgcn_perm(w3, w2, 0x05040100u));
+        const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07060302u),
+                                    __builtin_amdgcn_perm(w3, w2, 0x07060302u));
         *reinterpret_cast<uint2*>(&sm.t.vt[buf][8 * vc + 2 * jj][vpos]) = lo;
         *reinterpret_cast<uint2*>(&sm.t.vt[buf][8 * vc + 2 * jj + 1][vpos]) = hi;
       }
@@ -193,26 +200,32 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   };
 
   auto compute = [&](int buf, int vb) {
-    const int key0 = vb * BLK + 32 * kh;
-    if (key0 >= N) return;   // this wave's key half lies entirely past the sequence end
+    // Valid tile positions are [0, hi): only the last block can be ragged.
+    const int hi = min(BLK, N - vb * BLK);
+    const int p0 = 32 * kh;
+    if (hi <= p0) return;   // this wave's key half lies entirely past the sequence end
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[buf][32 * kh + r32][16 * ks + 8 * g]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[buf][p0 + r32][16 * ks + 8 * g]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
-    // s[i] is the logit of query row r32 for key 8*(i/4) + 4*g + i%4 of this half.
-    if (key0 + 32 > N) {
+    // s[i] is the logit of query row r32 for tile position p0 + 8*(i/4) + 4*g + i%4.
+    if (hi < p0 + 32) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key0 + 8 * (i >> 2) + 4 * g + (i & 3) >= N) s[i] = -INFINITY;
+        if (p0 + 8 * (i >> 2) + 4 * g + (i & 3) >= hi) s[i] = -INFINITY;
     }
-    float mx = s[0];
+    float mx = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), __builtin_fmaxf(s[2], s[3]));
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int i = 4; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[i], s[i + 1]));
+    {
+      // lanes l and l^32 hold the two 16-key halves of the same query row
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float mt = mx * c;
     if (__any(mt > m_run + RESCALE_SLACK)) {
       const float mn = fmaxf(m_run, mt);
@@ -225,13 +238,15 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
       m_run = mn;
     }
     float p[16];
-    float ls = 0.f;
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 16; i += 2) {
       p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
-      ls += p[i];
+      p[i + 1] = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -m_run));
+      ls0 += p[i];
+      ls1 += p[i + 1];
     }
-    l_part += ls;
+    l_part += ls0 + ls1;
     bf16x8 pb0, pb1;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -240,9 +255,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][32 * kh + 8 * g]);
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][p0 + 8 * g]);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, o[db], 0, 0, 0);
-      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][32 * kh + 16 + 8 * g]);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][p0 + 16 + 8 * g]);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, o[db], 0, 0, 0);
     }
   };
@@ -278,13 +293,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     __syncthreads();
     const int n = nlist;
     if (n == 0) continue;
-    gload(list[0]);
+    gload(__builtin_amdgcn_readfirstlane(list[0]));
     sstore(0);
     __syncthreads();
     for (int t = 0; t < n; ++t) {
-      const int vb = list[t];
+      const int vb = __builtin_amdgcn_readfirstlane(list[t]);
       const bool more = t + 1 < n;
-      if (more) gload(list[t + 1]);
+      if (more) gload(__builtin_amdgcn_readfirstlane(list[t + 1]));
       compute(t & 1, vb);
       if (more) sstore((t + 1) & 1);
       __syncthreads();
