@@ -15,9 +15,14 @@
 //    are lane-local plus one exchange with lane l^32.
 //  * The same 16 probabilities, rounded to bf16, are exactly the B operand of
 //    O^T += V^T P^T, provided the A operand (V^T) pairs each k-slot with the key
-//    the accumulator register held.  V is therefore stored transposed in LDS with
-//    the key index's bits 2 and 3 swapped; every operand read is then one 16-byte
-//    LDS load.
+//    the accumulator register held: four consecutive keys at one head-dim
+//    column per half operand.  V stays row-major in LDS and that operand is read
+//    with ds_read_b64_tr_b16, the gfx950 LDS transpose load: in each group of 16
+//    lanes, lanes 4r..4r+3 point at four 4-column pieces of key row base+r, and
+//    every lane receives the four keys at its own column.
+//  * K and V tiles are both fetched with the same contiguous pattern (each wave
+//    instruction reads 1 KB of consecutive rows) and written to LDS with 16-byte
+//    stores; no register shuffling of V is needed.
 //  * Kept K/V tiles stream through a 2-stage LDS ring: the next tile's global
 //    loads are issued before the current tile's math and written to the other
 //    stage after it, with one barrier per tile.
@@ -45,8 +50,7 @@ constexpr int BLK = 64;
 constexpr int NT = 256;
 constexpr int LIST_CAP = 2048;
 constexpr int CHUNK_WORDS = LIST_CAP / 64;
-constexpr int KPAD = 8;
-constexpr int VPAD = 8;
+constexpr int PAD = 16;       // bf16 elements of padding per LDS tile row
 constexpr float RESCALE_SLACK = 8.0f;
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family GPUs:
 // 32-bit data format, so the per-access range check against num_records applies.
@@ -54,8 +58,8 @@ constexpr int BUFFER_DWORD3 = 0x00020000;
 
 template <int D>
 struct __attribute__((aligned(16))) Tiles {
-  u16 k[2][BLK][D + KPAD];    // K tile, row-major
-  u16 vt[2][D][BLK + VPAD];   // V tile, transposed, key bits 2 and 3 swapped
+  u16 k[2][BLK][D + PAD];     // K tile, row-major
+  u16 v[2][BLK][D + PAD];     // V tile, row-major
 };
 
 template <int D>
@@ -71,8 +75,13 @@ union __attribute__((aligned(16))) Smem {
   Merge<D> mg;
 };
 
-__device__ __forceinline__ int swap_bits23(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read: see the file comment for the lane mapping.
+__device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(p));
 }
 
 template <int D>
@@ -81,8 +90,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int n_heads, int N,
     int nb, int W, float c, u16* __restrict__ O) {
   constexpr int CPR = D / 8;             // 16-byte chunks per token row
-  constexpr int KCH = BLK * CPR / NT;    // K chunks per thread
-  constexpr int V_THREADS = 16 * CPR;    // threads that stage V (4 keys x 8 dims each)
+  constexpr int KCH = BLK * CPR / NT;    // 16-byte chunks per thread, for K and for V
   constexpr int NDB = D / 32;            // 32-wide output column blocks
   constexpr int NKS = D / 16;            // k-steps of the QK^T contraction
 
@@ -135,69 +143,54 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  // Staging registers for the next tile (vector values, so they stay in VGPRs):
-  // K chunk r of this thread in dwords 4r..4r+3 of kreg, V key 4va+r in vreg.
-  static_assert(KCH <= 4, "K staging holds at most four 16-byte chunks");
-  u32x16 kreg = {};
-  u32x16 vreg = {};
-  const int va = tid & 15;       // 4-key group of the V tile this thread stages
-  const int vc = tid >> 4;       // 8-dim chunk of the V tile this thread stages
-  const int vpos = swap_bits23(4 * va);
-  constexpr bool ALL_STAGE_V = V_THREADS == NT;
+  // Two register staging sets hold the next two tiles in flight (vector values,
+  // so they stay in VGPRs): chunk r of this thread in dwords 4r..4r+3.
+  static_assert(KCH <= 4, "staging holds at most four 16-byte chunks per tensor");
+  struct Stage {
+    u32x16 k, v;
+  };
+  Stage sa = {}, sb = {};
 
   // Tiles are read with raw buffer loads: one descriptor per head, a scalar
   // byte offset for the tile and per-thread byte offsets fixed for the whole
-  // row.  The descriptor's range check returns zeros for rows at or past the
-  // sequence end (the ragged last block), which are masked out of the softmax.
+  // row (chunk tid + 256 r of the tile: every wave instruction covers 1 KB of
+  // consecutive bytes).  The descriptor's range check returns zeros for rows
+  // at or past the sequence end (the ragged last block), which are masked out
+  // of the softmax.
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)head_bytes, BUFFER_DWORD3);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Vh), 0, (int)head_bytes, BUFFER_DWORD3);
-  u32x4 koff = {}, voff = {};
-#pragma unroll
-  for (int r = 0; r < KCH; ++r) koff[r] = (uint32_t)((tid + NT * r) * 16);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = (uint32_t)(((4 * va + r) * CPR + vc) * 16);
 
-  auto gload = [&](int vb) {
+  auto gload = [&](Stage& st, int vb) {
     const int tile_off = vb * BLK * D * 2;
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)koff[r], tile_off, 0);
-      kreg[4 * r] = x[0]; kreg[4 * r + 1] = x[1]; kreg[4 * r + 2] = x[2]; kreg[4 * r + 3] = x[3];
-    }
-    if (ALL_STAGE_V || tid < V_THREADS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)voff[r], tile_off, 0);
-        vreg[4 * r] = x[0]; vreg[4 * r + 1] = x[1]; vreg[4 * r + 2] = x[2]; vreg[4 * r + 3] = x[3];
-      }
+      const int off = (tid + NT * r) * 16;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, tile_off, 0);
+      const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, tile_off, 0);
+      st.k[4 * r] = x[0]; st.k[4 * r + 1] = x[1]; st.k[4 * r + 2] = x[2]; st.k[4 * r + 3] = x[3];
+      st.v[4 * r] = y[0]; st.v[4 * r + 1] = y[1]; st.v[4 * r + 2] = y[2]; st.v[4 * r + 3] = y[3];
     }
   };
 
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
       const int ch = tid + NT * r;
       *reinterpret_cast<uint4*>(&sm.t.k[buf][ch / CPR][(ch % CPR) * 8]) =
-          make_uint4(kreg[4 * r], kreg[4 * r + 1], kreg[4 * r + 2], kreg[4 * r + 3]);
-    }
-    if (ALL_STAGE_V || tid < V_THREADS) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        // dims 8*vc + 2*jj (low halves) and 8*vc + 2*jj + 1 (high halves) of
-        // keys 4va..4va+3, packed two keys per dword with one byte permute each
-        const uint32_t w0 = vreg[jj], w1 = vreg[4 + jj], w2 = vreg[8 + jj], w3 = vreg[12 + jj];
-        const uint2 lo = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x05040100u),
-                                    __builtin_amdgcn_perm(w3, w2, 0x05040100u));
-        const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07060302u),
-                                    __builtin_amdgcn_perm(w3, w2, 0x07060302u));
-        *reinterpret_cast<uint2*>(&sm.t.vt[buf][8 * vc + 2 * jj][vpos]) = lo;
-        *reinterpret_cast<uint2*>(&sm.t.vt[buf][8 * vc + 2 * jj + 1][vpos]) = hi;
-      }
+          make_uint4(st.k[4 * r], st.k[4 * r + 1], st.k[4 * r + 2], st.k[4 * r + 3]);
+      *reinterpret_cast<uint4*>(&sm.t.v[buf][ch / CPR][(ch % CPR) * 8]) =
+          make_uint4(st.v[4 * r], st.v[4 * r + 1], st.v[4 * r + 2], st.v[4 * r + 3]);
     }
   };
+
+  // Per-lane pieces of the V^T operand: key row 4*g + (lane%16)/4 (+8 for the
+  // second half, +16 per k-step, +32*kh per key half) and column
+  // 16*((lane%32)/16) + 4*(lane%4) (+32 per output column block).
+  const int tr_row = 4 * g + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
 
   auto compute = [&](int buf, int vb) {
     // Valid tile positions are [0, hi): only the last block can be ragged.
@@ -255,10 +248,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][p0 + 8 * g]);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, o[db], 0, 0, 0);
-      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&sm.t.vt[buf][32 * db + r32][p0 + 16 + 8 * g]);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, o[db], 0, 0, 0);
+#pragma unroll
+      for (int s0 = 0; s0 < 2; ++s0) {
+        const u16* base = &sm.t.v[buf][p0 + 16 * s0 + tr_row][32 * db + tr_col];
+        const s16x4 lo = lds_read_tr16(base);
+        const s16x4 hi = lds_read_tr16(base + 8 * (D + PAD));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, s0 ? pb1 : pb0, o[db], 0, 0, 0);
+      }
     }
   };
 
@@ -293,16 +290,29 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     __syncthreads();
     const int n = nlist;
     if (n == 0) continue;
-    gload(__builtin_amdgcn_readfirstlane(list[0]));
-    sstore(0);
+    // Software pipeline, two tiles in flight: while tile t is computed from LDS
+    // stage t&1, tile t+1 sits in one register set (its loads issued a step
+    // earlier) and tile t+2's loads go out into the other.  The loop body is
+    // written twice so each step names its register sets statically.  Loads
+    // are issued on every step (past the end of the list the last tile is
+    // fetched again) so the number of loads in flight is the same on every
+    // path and each LDS store waits only for its own, older, loads.
+    auto tile = [&](int t) { return __builtin_amdgcn_readfirstlane(list[min(t, n - 1)]); };
+    gload(sa, tile(0));
+    sstore(sa, 0);
+    gload(sb, tile(1));
     __syncthreads();
-    for (int t = 0; t < n; ++t) {
-      const int vb = __builtin_amdgcn_readfirstlane(list[t]);
-      const bool more = t + 1 < n;
-      if (more) gload(__builtin_amdgcn_readfirstlane(list[t + 1]));
-      compute(t & 1, vb);
-      if (more) sstore((t + 1) & 1);
+    for (int t = 0;;) {
+      gload(sa, tile(t + 2));
+      compute(0, tile(t));
+      if (t + 1 < n) sstore(sb, 1);
       __syncthreads();
+      if (++t >= n) break;
+      gload(sb, tile(t + 2));
+      compute(1, tile(t));
+      if (t + 1 < n) sstore(sa, 0);
+      __syncthreads();
+      if (++t >= n) break;
     }
   }
 
