@@ -140,16 +140,19 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = -INFINITY;
+  // Running max in the exp2 domain.  It starts at a large finite value instead
+  // of -inf so a tile whose keys are all masked for this wave yields
+  // exp2(-inf) = 0 everywhere without a special case.
+  float m_run = -1.0e30f;
   float l_part = 0.f;
 
-  // Two register staging sets hold the next two tiles in flight (vector values,
-  // so they stay in VGPRs): chunk r of this thread in dwords 4r..4r+3.
+  // Register staging for the tiles in flight (vector values, so they stay in
+  // VGPRs): chunk r of this thread in dwords 4r..4r+3.
   static_assert(KCH <= 4, "staging holds at most four 16-byte chunks per tensor");
   struct Stage {
     u32x16 k, v;
   };
-  Stage sa = {}, sb = {};
+  Stage st = {};
 
   // Tiles are read with raw buffer loads: one descriptor per head, a scalar
   // byte offset for the tile and per-thread byte offsets fixed for the whole
@@ -163,25 +166,32 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Vh), 0, (int)head_bytes, BUFFER_DWORD3);
 
-  auto gload = [&](Stage& st, int vb) {
-    const int tile_off = vb * BLK * D * 2;
+  auto gload = [&](int kvb, int vvb) {
+    const int ktile_off = kvb * BLK * D * 2;
+    const int vtile_off = vvb * BLK * D * 2;
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
       const int off = (tid + NT * r) * 16;
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, tile_off, 0);
-      const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, tile_off, 0);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, ktile_off, 0);
+      const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, vtile_off, 0);
       st.k[4 * r] = x[0]; st.k[4 * r + 1] = x[1]; st.k[4 * r + 2] = x[2]; st.k[4 * r + 3] = x[3];
       st.v[4 * r] = y[0]; st.v[4 * r + 1] = y[1]; st.v[4 * r + 2] = y[2]; st.v[4 * r + 3] = y[3];
     }
   };
 
-  auto sstore = [&](const Stage& st, int buf) {
+  auto sstore_k = [&](int kbuf) {
 #pragma unroll
     for (int r = 0; r < KCH; ++r) {
       const int ch = tid + NT * r;
-      *reinterpret_cast<uint4*>(&sm.t.k[buf][ch / CPR][(ch % CPR) * 8]) =
+      *reinterpret_cast<uint4*>(&sm.t.k[kbuf][ch / CPR][(ch % CPR) * 8]) =
           make_uint4(st.k[4 * r], st.k[4 * r + 1], st.k[4 * r + 2], st.k[4 * r + 3]);
-      *reinterpret_cast<uint4*>(&sm.t.v[buf][ch / CPR][(ch % CPR) * 8]) =
+    }
+  };
+  auto sstore_v = [&](int vbuf) {
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int ch = tid + NT * r;
+      *reinterpret_cast<uint4*>(&sm.t.v[vbuf][ch / CPR][(ch % CPR) * 8]) =
           make_uint4(st.v[4 * r], st.v[4 * r + 1], st.v[4 * r + 2], st.v[4 * r + 3]);
     }
   };
@@ -189,27 +199,24 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   // Per-lane pieces of the V^T operand: key row 4*g + (lane%16)/4 (+8 for the
   // second half, +16 per k-step, +32*kh per key half) and column
   // 16*((lane%32)/16) + 4*(lane%4) (+32 per output column block).
+  const int p0 = 32 * kh;         // first tile position of this wave's key half
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
 
-  auto compute = [&](int buf, int vb) {
-    // Valid tile positions are [0, hi): only the last block can be ragged.
-    const int hi = min(BLK, N - vb * BLK);
-    const int p0 = 32 * kh;
-    if (hi <= p0) return;   // this wave's key half lies entirely past the sequence end
-    f32x16 s;
+  // One pipeline step for this wave: online softmax of S (tile vb, already in
+  // registers), the QK^T MFMAs of the next tile from K stage kbuf (returned),
+  // and O^T += V^T P^T from V stage vbuf.  The next tile's MFMAs do not depend on
+  // the softmax, so they are issued in the same straight-line block as the
+  // exponentials and interleaved with them (one MFMA, then a few VALU ops).
+  // s[i] is the logit of query row r32 for tile position p0 + 8*(i/4) + 4*g + i%4.
+  auto step = [&](f32x16 s, int vb, int kbuf, int vbuf, bool may_be_ragged) {
+    if (may_be_ragged) {
+      const int hi = N - vb * BLK;   // tile positions >= hi lie past the sequence end
+      if (hi < p0 + 32) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[buf][p0 + r32][16 * ks + 8 * g]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-    }
-    // s[i] is the logit of query row r32 for tile position p0 + 8*(i/4) + 4*g + i%4.
-    if (hi < p0 + 32) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (p0 + 8 * (i >> 2) + 4 * g + (i & 3) >= hi) s[i] = -INFINITY;
+        for (int i = 0; i < 16; ++i)
+          if (p0 + 8 * (i >> 2) + 4 * g + (i & 3) >= hi) s[i] = -INFINITY;
+      }
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), __builtin_fmaxf(s[2], s[3]));
 #pragma unroll
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    const float mt = mx * c;
+    const float mt = mx * c;       // -inf when every key of this half is masked
     if (__any(mt > m_run + RESCALE_SLACK)) {
       const float mn = fmaxf(m_run, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
@@ -230,14 +237,36 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       m_run = mn;
     }
+    // --- straight-line block: next tile's QK^T interleaved with this tile's exp2
+    f32x16 sn;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sn[i] = 0.f;
     float p[16];
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[kbuf][p0 + r32][16 * ks + 8 * g]);
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sn, 0, 0, 0);
+      if (2 * ks < 16) {
+        const int i = 2 * ks;
+        p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
+        p[i + 1] = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -m_run));
+        ls0 += p[i];
+        ls1 += p[i + 1];
+      }
+    }
+#pragma unroll
+    for (int i = 2 * NKS; i < 16; i += 2) {
       p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
       p[i + 1] = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -m_run));
       ls0 += p[i];
       ls1 += p[i + 1];
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the K operand read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU ops
     }
     l_part += ls0 + ls1;
     bf16x8 pb0, pb1;
@@ -250,13 +279,27 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int s0 = 0; s0 < 2; ++s0) {
-        const u16* base = &sm.t.v[buf][p0 + 16 * s0 + tr_row][32 * db + tr_col];
+        const u16* base = &sm.t.v[vbuf][p0 + 16 * s0 + tr_row][32 * db + tr_col];
         const s16x4 lo = lds_read_tr16(base);
-        const s16x4 hi = lds_read_tr16(base + 8 * (D + PAD));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const s16x4 hi2 = lds_read_tr16(base + 8 * (D + PAD));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, s0 ? pb1 : pb0, o[db], 0, 0, 0);
       }
     }
+    return sn;
+  };
+
+  // S^T of the first tile of a list (no softmax work to overlap with).
+  auto qk = [&](int kbuf) {
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[kbuf][p0 + r32][16 * ks + 8 * g]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+    }
+    return s;
   };
 
   const int tail_bits = nb & 63;
@@ -290,29 +333,30 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     __syncthreads();
     const int n = nlist;
     if (n == 0) continue;
-    // Software pipeline, two tiles in flight: while tile t is computed from LDS
-    // stage t&1, tile t+1 sits in one register set (its loads issued a step
-    // earlier) and tile t+2's loads go out into the other.  The loop body is
-    // written twice so each step names its register sets statically.  Loads
-    // are issued on every step (past the end of the list the last tile is
-    // fetched again) so the number of loads in flight is the same on every
-    // path and each LDS store waits only for its own, older, loads.
+    // Software pipeline with K one tile ahead of V.  At the top of step t the K
+    // stage (t+1)&1 holds K(t+1), the V stage t&1 holds V(t), and S(t) is in
+    // registers.  Step t issues the loads of K(t+2) and V(t+1), runs the QK^T
+    // MFMAs of tile t+1 next to the softmax of tile t (independent work the
+    // scheduler can interleave), then PV of tile t, and stores K(t+2), V(t+1)
+    // into the stages just freed.  Past the end of the list the last tile is
+    // used again (loads stay unconditional; the extra S is discarded).
     auto tile = [&](int t) { return __builtin_amdgcn_readfirstlane(list[min(t, n - 1)]); };
-    gload(sa, tile(0));
-    sstore(sa, 0);
-    gload(sb, tile(1));
+    gload(tile(0), tile(0));
+    sstore_k(0);
+    sstore_v(0);
     __syncthreads();
-    for (int t = 0;;) {
-      gload(sa, tile(t + 2));
-      compute(0, tile(t));
-      if (t + 1 < n) sstore(sb, 1);
+    gload(tile(1), tile(1));
+    f32x16 s_cur = qk(0);
+    sstore_k(1);
+    __syncthreads();
+    // only the last block of the sequence can be ragged, and it is always the
+    // last entry of an ascending list
+    for (int t = 0; t < n; ++t) {
+      gload(tile(t + 2), tile(t + 1));
+      s_cur = step(s_cur, tile(t), (t + 1) & 1, t & 1, t == n - 1);
+      sstore_k(t & 1);
+      sstore_v((t + 1) & 1);
       __syncthreads();
-      if (++t >= n) break;
-      gload(sb, tile(t + 2));
-      compute(1, tile(t));
-      if (t + 1 < n) sstore(sa, 0);
-      __syncthreads();
-      if (++t >= n) break;
     }
   }
 
