@@ -3,9 +3,11 @@
 // The packed row mask (ScalingAttention, section 4.3.2) already tells how many
 // kept tiles each (head, query block) row will run; a popcount pass turns that
 // into a schedule.  Heads run in decreasing total work so the heaviest heads are
-// dispatched first and the lightest fill the tail; within a head, query blocks
-// stay in order so that concurrently resident workgroups of one head share
-// that head's K/V in the caches.
+// dispatched first and the lightest fill the tail.  Within a head, rows run in
+// decreasing kept-block count: the workgroups resident at the same time then
+// hold rows of nearly equal length, start together, walk their ascending tile
+// lists at the same pace and finish together, so tiles one of them fetches are
+// still in the XCD's L2 when the others ask for them.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -30,11 +32,16 @@ __global__ void row_counts_kernel(const uint64_t* __restrict__ mask, int n_rows,
 }
 
 // One workgroup per head: rank the head among all heads (more work first, ties
-// by head index) and write its rows at that rank's slot of the order.
+// by head index), then rank each of its rows within the head (more kept blocks
+// first, ties by query block) and write row ids at those positions.
+constexpr int SORT_MAX_NB = 8192;   // rows per head ranked in LDS; longer heads keep u order
+
 __global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restrict__ head_tiles,
+                                                         const int32_t* __restrict__ counts,
                                                          int n_heads, int nb,
                                                          int32_t* __restrict__ order) {
   __shared__ int partial[256];
+  __shared__ int cnt[SORT_MAX_NB];
   const int h = blockIdx.x;
   const int64_t mine = head_tiles[h];
   int before = 0;
@@ -43,13 +50,28 @@ __global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restri
     before += (t > mine) || (t == mine && j < h);
   }
   partial[threadIdx.x] = before;
+  const bool sort_rows = nb <= SORT_MAX_NB;
+  if (sort_rows)
+    for (int u = threadIdx.x; u < nb; u += blockDim.x) cnt[u] = counts[(size_t)h * nb + u];
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) partial[threadIdx.x] += partial[threadIdx.x + s];
     __syncthreads();
   }
   const int rank = partial[0];
-  for (int u = threadIdx.x; u < nb; u += blockDim.x) order[(size_t)rank * nb + u] = h * nb + u;
+  int32_t* dst = order + (size_t)rank * nb;
+  for (int u = threadIdx.x; u < nb; u += blockDim.x) {
+    int r = u;
+    if (sort_rows) {
+      const int cu = cnt[u];
+      r = 0;
+      for (int j = 0; j < nb; ++j) {
+        const int cj = cnt[j];
+        r += (cj > cu) || (cj == cu && j < u);
+      }
+    }
+    dst[r] = h * nb + u;
+  }
 }
 
 }  // namespace
@@ -67,8 +89,8 @@ int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts,
   hipLaunchKernelGGL(row_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, mask, rows,
                      nb, W, lastmask, counts, head_tiles);
   BSA_CHECK_HIP(hipGetLastError());
-  hipLaunchKernelGGL(head_order_kernel, dim3(n_heads), dim3(256), 0, stream, head_tiles, n_heads,
-                     nb, order);
+  hipLaunchKernelGGL(head_order_kernel, dim3(n_heads), dim3(256), 0, stream, head_tiles, counts,
+                     n_heads, nb, order);
   BSA_CHECK_HIP(hipGetLastError());
   return ok();
 }

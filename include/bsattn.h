@@ -72,8 +72,8 @@ int bsa_mask_words(int seq_len, int block);
  *   scale      finite and > 0 (typically 1/sqrt(head_dim));
  *   out        bf16 [n_heads][seq_len][head_dim], written (round to nearest even).
  *
- * Work is ordered by a device-side planning pass (row popcounts, heads in
- * decreasing kept-block count) kept in a library-owned per-device scratch buffer
+ * Work is ordered by a device-side planning pass (row popcounts; heads, then rows,
+ * in decreasing kept-block count) kept in a library-owned per-device scratch buffer
  * that grows on demand; calls that overlap on one device from different streams
  * race on that buffer -- use sparse_attn_plan + sparse_attn_fwd_planned with
  * caller-owned buffers for concurrent use.
@@ -99,8 +99,10 @@ int sparse_attn_fwd_f32(const float* q, const float* k, const float* v, const ui
  *   row_counts  int32 [n_heads * nb], written: kept blocks of each (head, query block) row.
  *   head_tiles  int64 [n_heads], written: kept blocks of each head.
  *   work_order  int32 [n_heads * nb], written: a permutation of row ids (h * nb + u):
- *               heads in decreasing head_tiles (ties by head index), rows of one head
- *               in increasing u.
+ *               heads in decreasing head_tiles (ties by head index); within a head,
+ *               rows in decreasing row_counts (ties by increasing u) when nb <= 8192,
+ *               else in increasing u.  Rows of equal length then run side by side,
+ *               which keeps their tile walks in step and their K/V in the L2 cache.
  */
 int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int block,
                      int32_t* row_counts, int64_t* head_tiles, int32_t* work_order,

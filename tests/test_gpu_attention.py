@@ -172,10 +172,12 @@ def test_plan_order_is_heads_by_decreasing_work():
     counts, tiles, order = bsa.plan(gu.to_dev(crm.pack_rows(keep)), n)
     torch.cuda.synchronize()
     t = keep.reshape(H, -1).sum(1)
+    rc = keep.sum(2)
     heads = sorted(range(H), key=lambda h: (-t[h], h))
-    want = np.concatenate([np.arange(nb) + h * nb for h in heads])
+    want = np.concatenate([h * nb + np.array(sorted(range(nb), key=lambda u: (-rc[h, u], u))) for h in heads])
     assert np.array_equal(order.cpu().numpy(), want)
     assert np.array_equal(tiles.cpu().numpy(), t)
+    assert np.array_equal(counts.cpu().numpy(), rc.reshape(-1))
 
 
 def test_rows_beyond_one_decode_chunk():
