@@ -15,14 +15,14 @@
 //    are lane-local plus one exchange with lane l^32.
 //  * The same 16 probabilities, rounded to bf16, are exactly the B operand of
 //    O^T += V^T P^T, provided the A operand (V^T) pairs each k-slot with the key
-//    the accumulator register held: four consecutive keys at one head-dim
-//    column per half operand.  V stays row-major in LDS and that operand is read
-//    with ds_read_b64_tr_b16, the gfx950 LDS transpose load: in each group of 16
-//    lanes, lanes 4r..4r+3 point at four 4-column pieces of key row base+r, and
-//    every lane receives the four keys at its own column.
-//  * K and V tiles are both fetched with the same contiguous pattern (each wave
-//    instruction reads 1 KB of consecutive rows) and written to LDS with 16-byte
-//    stores; no register shuffling of V is needed.
+//    the accumulator register held.  Tiles are fetched with a contiguous pattern
+//    (each wave instruction reads 1 KB), which gives every loader thread one
+//    8-dim chunk of keys a, a+16, a+32, a+48.  K rows are placed in LDS in a
+//    permuted key order and V is written transposed (d-major) so that those four
+//    keys form one 8-byte run at positions that line up with four consecutive
+//    MFMA k-slots; every MFMA operand is then a single 16-byte LDS read.  The
+//    transposed V rows have their 16-byte chunks XOR-swizzled by (d >> 4) & 7 so
+//    both the 8-byte writes and the 16-byte reads avoid LDS bank conflicts.
 //  * Kept K/V tiles stream through a 2-stage LDS ring: the next tile's global
 //    loads are issued before the current tile's math and written to the other
 //    stage after it, with one barrier per tile.
@@ -50,7 +50,8 @@ constexpr int BLK = 64;
 constexpr int NT = 256;
 constexpr int LIST_CAP = 2048;
 constexpr int CHUNK_WORDS = LIST_CAP / 64;
-constexpr int PAD = 16;       // bf16 elements of padding per LDS tile row
+constexpr int KPAD = 8;       // bf16 elements of padding per LDS K row
+constexpr int VPAD = 8;       // bf16 elements of padding per LDS V^T row
 constexpr float RESCALE_SLACK = 8.0f;
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family GPUs:
 // 32-bit data format, so the per-access range check against num_records applies.
@@ -58,8 +59,8 @@ constexpr int BUFFER_DWORD3 = 0x00020000;
 
 template <int D>
 struct __attribute__((aligned(16))) Tiles {
-  u16 k[2][BLK][D + PAD];     // K tile, row-major
-  u16 v[2][BLK][D + PAD];     // V tile, row-major
+  u16 k[2][BLK][D + KPAD];    // K tile; row R holds key key_of_row(R)
+  u16 vt[2][D][BLK + VPAD];   // V tile transposed, chunks swizzled (see file comment)
 };
 
 template <int D>
@@ -75,14 +76,21 @@ union __attribute__((aligned(16))) Smem {
   Merge<D> mg;
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposing LDS read: see the file comment for the lane mapping.
-__device__ __forceinline__ s16x4 lds_read_tr16(const u16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(__attribute__((address_space(3))) void*)(p));
+// Key order inside a tile.  A loader thread holds keys a + 16 j (a < 16,
+// j < 4).  Key a + 16 j goes to K row 32(a>>3) + 16((a>>2)&1) + 8((a>>1)&1) +
+// 4(a&1) + j, and to V^T positions pos0(a) + j with
+// pos0(a) = 32(a>>3) + 16((a>>2)&1) + 8(a&1) + 4((a>>1)&1).  With this pair of
+// maps the k-slot j of the PV operand read at positions 32kh + 16s + 8g .. +7
+// holds the key whose logit sits in accumulator register 8s + j of the QK^T
+// MFMA that read K rows 32kh .. 32kh + 31 (lane group g).
+__device__ __forceinline__ int k_row_base(int a) {
+  return 32 * (a >> 3) + 16 * ((a >> 2) & 1) + 8 * ((a >> 1) & 1) + 4 * (a & 1);
 }
+__device__ __forceinline__ int vt_pos_base(int a) {
+  return 32 * (a >> 3) + 16 * ((a >> 2) & 1) + 8 * (a & 1) + 4 * ((a >> 1) & 1);
+}
+// 16-byte chunk swizzle of V^T row d
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 4) & 7; }
 
 template <int D>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
@@ -147,19 +155,29 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   float l_part = 0.f;
 
   // Register staging for the tiles in flight (vector values, so they stay in
-  // VGPRs): chunk r of this thread in dwords 4r..4r+3.
-  static_assert(KCH <= 4, "staging holds at most four 16-byte chunks per tensor");
+  // VGPRs): chunk j of this thread in dwords 4j..4j+3.
   struct Stage {
     u32x16 k, v;
   };
   Stage st = {};
 
+  // Loader threads: LT threads per tensor, each loading chunk cc (8 dims) of keys
+  // a + 16 j, j = 0..3 -- chunk index t' + LT j of the tile, so each wave
+  // instruction covers 1 KB of consecutive bytes.  For d = 128 every thread
+  // loads both tensors; for d = 64 the lower half loads V and the upper half K.
+  constexpr int LT = 16 * CPR;
+  static_assert(LT == NT || 2 * LT == NT, "loader split");
+  const bool v_loader = LT == NT || tid < LT;
+  const bool k_loader = LT == NT || tid >= NT - LT;
+  const int kt = LT == NT ? tid : tid - (NT - LT);
+  const int vt_ = tid;
+  const int ka = kt / CPR, kcc = kt % CPR;
+  const int va = vt_ / CPR, vcc = vt_ % CPR;
+
   // Tiles are read with raw buffer loads: one descriptor per head, a scalar
   // byte offset for the tile and per-thread byte offsets fixed for the whole
-  // row (chunk tid + 256 r of the tile: every wave instruction covers 1 KB of
-  // consecutive bytes).  The descriptor's range check returns zeros for rows
-  // at or past the sequence end (the ragged last block), which are masked out
-  // of the softmax.
+  // row.  The descriptor's range check returns zeros for rows at or past the
+  // sequence end (the ragged last block), which are masked out of the softmax.
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)head_bytes, BUFFER_DWORD3);
@@ -169,53 +187,67 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   auto gload = [&](int kvb, int vvb) {
     const int ktile_off = kvb * BLK * D * 2;
     const int vtile_off = vvb * BLK * D * 2;
+    if (k_loader) {
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int off = (tid + NT * r) * 16;
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, ktile_off, 0);
-      const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, vtile_off, 0);
-      st.k[4 * r] = x[0]; st.k[4 * r + 1] = x[1]; st.k[4 * r + 2] = x[2]; st.k[4 * r + 3] = x[3];
-      st.v[4 * r] = y[0]; st.v[4 * r + 1] = y[1]; st.v[4 * r + 2] = y[2]; st.v[4 * r + 3] = y[3];
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, (kt + LT * j) * 16, ktile_off, 0);
+        st.k[4 * j] = x[0]; st.k[4 * j + 1] = x[1]; st.k[4 * j + 2] = x[2]; st.k[4 * j + 3] = x[3];
+      }
+    }
+    if (v_loader) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, (vt_ + LT * j) * 16, vtile_off, 0);
+        st.v[4 * j] = y[0]; st.v[4 * j + 1] = y[1]; st.v[4 * j + 2] = y[2]; st.v[4 * j + 3] = y[3];
+      }
     }
   };
 
+  const int k_row0 = k_row_base(ka);
   auto sstore_k = [&](int kbuf) {
+    if (k_loader) {
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int ch = tid + NT * r;
-      *reinterpret_cast<uint4*>(&sm.t.k[kbuf][ch / CPR][(ch % CPR) * 8]) =
-          make_uint4(st.k[4 * r], st.k[4 * r + 1], st.k[4 * r + 2], st.k[4 * r + 3]);
-    }
-  };
-  auto sstore_v = [&](int vbuf) {
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int ch = tid + NT * r;
-      *reinterpret_cast<uint4*>(&sm.t.v[vbuf][ch / CPR][(ch % CPR) * 8]) =
-          make_uint4(st.v[4 * r], st.v[4 * r + 1], st.v[4 * r + 2], st.v[4 * r + 3]);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(&sm.t.k[kbuf][k_row0 + j][8 * kcc]) =
+            make_uint4(st.k[4 * j], st.k[4 * j + 1], st.k[4 * j + 2], st.k[4 * j + 3]);
     }
   };
 
-  // Per-lane pieces of the V^T operand: key row 4*g + (lane%16)/4 (+8 for the
-  // second half, +16 per k-step, +32*kh per key half) and column
-  // 16*((lane%32)/16) + 4*(lane%4) (+32 per output column block).
-  const int p0 = 32 * kh;         // first tile position of this wave's key half
-  const int tr_row = 4 * g + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
+  // V^T writes: for each of the thread's 8 dims, the values of its 4 keys as one
+  // 8-byte run; two keys per dword assembled with one byte permute.
+  const int vpos = vt_pos_base(va);
+  const int vcol = 8 * ((vpos >> 3) ^ vt_swz(8 * vcc)) + (vpos & 4);
+  auto sstore_v = [&](int vbuf) {
+    if (v_loader) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t w0 = st.v[e >> 1], w1 = st.v[4 + (e >> 1)];
+        const uint32_t w2 = st.v[8 + (e >> 1)], w3 = st.v[12 + (e >> 1)];
+        *reinterpret_cast<uint2*>(&sm.t.vt[vbuf][8 * vcc + e][vcol]) =
+            make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
+      }
+    }
+  };
+
+  const int p0 = 32 * kh;         // first K row of this wave's key half
 
   // One pipeline step for this wave: online softmax of S (tile vb, already in
   // registers), the QK^T MFMAs of the next tile from K stage kbuf (returned),
   // and O^T += V^T P^T from V stage vbuf.  The next tile's MFMAs do not depend on
   // the softmax, so they are issued in the same straight-line block as the
   // exponentials and interleaved with them (one MFMA, then a few VALU ops).
-  // s[i] is the logit of query row r32 for tile position p0 + 8*(i/4) + 4*g + i%4.
+  // s[i] is the logit of query row r32 for the key held by K row
+  // p0 + 8*(i/4) + 4*g + i%4, i.e. key 8kh + 4(i>>3) + 2((i>>2)&1) + g + 16(i&3).
   auto step = [&](f32x16 s, int vb, int kbuf, int vbuf, bool may_be_ragged) {
     if (may_be_ragged) {
       const int hi = N - vb * BLK;   // tile positions >= hi lie past the sequence end
-      if (hi < p0 + 32) {
+      if (hi < BLK) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (p0 + 8 * (i >> 2) + 4 * g + (i & 3) >= hi) s[i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int key = 8 * kh + 4 * (i >> 3) + 2 * ((i >> 2) & 1) + g + 16 * (i & 3);
+          if (key >= hi) s[i] = -INFINITY;
+        }
       }
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), __builtin_fmaxf(s[2], s[3]));
@@ -277,12 +309,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * db + r32;
 #pragma unroll
       for (int s0 = 0; s0 < 2; ++s0) {
-        const u16* base = &sm.t.v[vbuf][p0 + 16 * s0 + tr_row][32 * db + tr_col];
-        const s16x4 lo = lds_read_tr16(base);
-        const s16x4 hi2 = lds_read_tr16(base + 8 * (D + PAD));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+        const int chunk = (4 * kh + 2 * s0 + g) ^ vt_swz(d);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.vt[vbuf][d][8 * chunk]);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, s0 ? pb1 : pb0, o[db], 0, 0, 0);
       }
     }
