@@ -53,41 +53,19 @@ constexpr int BLK = 64;
 constexpr int NT = 256;
 constexpr int LIST_CAP = 2048;
 constexpr int CHUNK_WORDS = LIST_CAP / 64;
-constexpr int KPAD = 8;       // bf16 elements of padding per LDS K row
 constexpr float RESCALE_SLACK = 8.0f;
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family GPUs:
 // 32-bit data format, so the per-access range check against num_records applies.
 constexpr int BUFFER_DWORD3 = 0x00020000;
 
-template <int D>
-struct __attribute__((aligned(16))) Tiles {
-  u16 k[2][BLK][D + KPAD];    // K tile; row R holds key key_of_row(R)
-  u16 vt[2][D][BLK];          // V tile transposed, 16-byte chunks swizzled by vt_swz
-};
-
-template <int D>
-struct __attribute__((aligned(16))) Merge {
-  float o[2][D / 2][64];      // [query-row half][accumulator register][lane]
-  float m[2][32];
-  float l[2][32];
-};
-
-template <int D>
-union __attribute__((aligned(16))) Smem {
-  Tiles<D> t;
-  Merge<D> mg;
-};
-
-// Key order inside a tile.  A loader thread holds keys a + 16 j (a < 16,
-// j < 4).  Key a + 16 j goes to K row 32(a>>3) + 16((a>>2)&1) + 8((a>>1)&1) +
-// 4(a&1) + j, and to V^T positions pos0(a) + j with
+// Key order inside a tile.  Key a + 16 j (a < 16, j < 4) goes to K row 4a + j
+// and to V^T positions pos0(a) + j with
 // pos0(a) = 32(a>>3) + 16((a>>2)&1) + 8(a&1) + 4((a>>1)&1).  With this pair of
 // maps the k-slot j of the PV operand read at positions 32kh + 16s + 8g .. +7
 // holds the key whose logit sits in accumulator register 8s + j of the QK^T
 // MFMA that read K rows 32kh .. 32kh + 31 (lane group g).
-__device__ __forceinline__ int k_row_base(int a) {
-  return 32 * (a >> 3) + 16 * ((a >> 2) & 1) + 8 * ((a >> 1) & 1) + 4 * (a & 1);
-}
+// (The K row map is simply 4a + j; the inverse gives the key of a row.)
+__device__ __forceinline__ int key_of_row(int r) { return (r >> 2) + 16 * (r & 3); }
 __device__ __forceinline__ int vt_pos_base(int a) {
   return 32 * (a >> 3) + 16 * ((a >> 2) & 1) + 8 * (a & 1) + 4 * ((a >> 1) & 1);
 }
@@ -98,6 +76,16 @@ __device__ __forceinline__ int vt_pos_base(int a) {
 // over 32 banks.  V^T rows are 128 bytes, unpadded, and the 16-byte chunk c of
 // row d is stored at chunk c ^ vt_swz(d).  Together with the loader lane maps
 // below, every operand read and every transposing write is conflict free.
+// K rows are D * 2 bytes, unpadded (the tile arrives by LDS DMA, which writes
+// 1 KB runs), and chunk c of row r is stored at chunk c ^ k_swz(r): the rows a
+// read pass touches then land on distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  if constexpr (D == 128)
+    return r & 15;
+  else
+    return (r >> 1) & 7;
+}
 __device__ __forceinline__ int vt_swz(int d) {
   return (((d >> 1) ^ (d >> 5)) & 1) | (((d >> 4) & 1) << 1) | (((d >> 3) & 1) << 2);
 }
@@ -122,16 +110,24 @@ __device__ __forceinline__ void v_loader_map(int tid, int& a, int& vcc) {
 template <int D>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int n_heads, int N,
-    int nb, int W, float c, u16* __restrict__ O) {
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int wg_offset,
+    int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
   constexpr int CPR = D / 8;             // 16-byte chunks per token row
   constexpr int KCH = BLK * CPR / NT;    // 16-byte chunks per thread, for K and for V
   constexpr int NDB = D / 32;            // 32-wide output column blocks
   constexpr int NKS = D / 16;            // k-steps of the QK^T contraction
 
-  __shared__ Smem<D> sm;
-  __shared__ u16 list[LIST_CAP];
+  // LDS.  The two K stages are separate objects so the compiler can tell the
+  // stage being filled by DMA from the stage being read, and waits for a DMA
+  // only where its own stage is read.  After the tile loop the V^T stages hold
+  // the merge of the two key halves' accumulators and the list holds their
+  // running max and sum.
+  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];   // K stage 0; row r holds key_of_row(r)
+  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];   // K stage 1
+  __shared__ __attribute__((aligned(16))) u16 vts[2][D][BLK];  // V^T stages, chunks swizzled by vt_swz
+  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
   __shared__ int nlist;
+  auto kstage = [&](int b) { return b ? kst1 : kst0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,9 +137,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  int row_id = blockIdx.x;
+  int row_id = wg_offset + blockIdx.x;
   if (order) {
-    row_id = order[blockIdx.x];
+    row_id = order[row_id];
     if (row_id < 0 || row_id >= n_heads * nb) return;
   }
   const int h = row_id / nb;
@@ -181,26 +177,46 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   float m_run = -1.0e30f;
   float l_part = 0.f;
 
-  // Register staging for the tiles in flight (vector values, so they stay in
-  // VGPRs): chunk j of this thread in dwords 4j..4j+3.
-  struct Stage {
-    u32x16 k, v;
-  };
-  Stage st = {};
+  // Register staging for the V tiles in flight, two deep (vector values, so
+  // they stay in VGPRs): chunk j of this thread in dwords 4j..4j+3.
+  u32x16 vst[2] = {};
 
-  // Loader threads: LT threads per tensor, each loading one 8-dim chunk of keys
-  // a + 16 j, j = 0..3, so each wave instruction covers 1 KB of consecutive
-  // bytes (K threads in linear order, V threads in the order of v_loader_map).
-  // For d = 128 every thread loads both tensors; for d = 64 the lower half loads
-  // V and the upper half K.
+  // V loader threads: LT threads, each loading one 8-dim chunk of keys a + 16 j,
+  // j = 0..3, in the lane order of v_loader_map; each wave instruction covers
+  // 1 KB of consecutive bytes.  For d = 128 every thread loads V; for d = 64
+  // the lower half does and the upper half issues the K DMA.
   constexpr int LT = 16 * CPR;
   static_assert(LT == NT || 2 * LT == NT, "loader split");
   const bool v_loader = LT == NT || tid < LT;
-  const bool k_loader = LT == NT || tid >= NT - LT;
-  const int kt = LT == NT ? tid : tid - (NT - LT);
-  const int ka = kt / CPR, kcc = kt % CPR;
   int va, vcc;
   v_loader_map<D>(tid, va, vcc);
+
+  // K tiles travel by LDS DMA (global -> LDS without VGPRs).  One wave
+  // instruction writes 1 KB = KR consecutive K rows; lane l fills row
+  // R0 + l / CPR at chunk position l % CPR, so it fetches the key of that row
+  // at the chunk the swizzle stores there.
+  constexpr int KR = 1024 / (2 * D);                  // K rows per DMA instruction
+  constexpr int KWAVES = LT == NT ? 4 : 2;            // waves issuing the K DMA
+  constexpr int KI = BLK / (KR * KWAVES);             // DMA instructions per wave
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool k_dma_wave = LT == NT || wave_u >= 2;
+  const int kw = LT == NT ? wave_u : wave_u - 2;
+  int k_voff[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int r = (kw * KI + i) * KR + lane / CPR;
+    const int c = (lane % CPR) ^ k_swz<D>(r);
+    k_voff[i] = (key_of_row(r) * CPR + c) * 16;
+  }
+  // Byte offsets (within a K stage) of this lane's QK^T A operands: row
+  // p0 + r32, logical chunk 2 ks + g.
+  const int p0 = 32 * kh;         // first K row of this wave's key half
+  int k_rd[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int r = p0 + r32;
+    k_rd[ks] = r * D * 2 + 16 * ((2 * ks + g) ^ k_swz<D>(r));
+  }
 
   // Tiles are read with raw buffer loads: one descriptor per head, a scalar
   // byte offset for the tile and per-thread byte offsets fixed for the whole
@@ -212,54 +228,60 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Vh), 0, (int)head_bytes, BUFFER_DWORD3);
 
-  auto gload = [&](int kvb, int vvb) {
-    const int ktile_off = kvb * BLK * D * 2;
-    const int vtile_off = vvb * BLK * D * 2;
-    if (k_loader) {
+  auto kdma = [&](int kvb, int kbuf) {
+    if (k_dma_wave) {
+      const int ktile_off = kvb * BLK * D * 2;
+#ifdef __HIP_DEVICE_COMPILE__   // the host pass cannot form LDS address-space pointers
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, (kt + LT * j) * 16, ktile_off, 0);
-        st.k[4 * j] = x[0]; st.k[4 * j + 1] = x[1]; st.k[4 * j + 2] = x[2]; st.k[4 * j + 3] = x[3];
-      }
+      for (int i = 0; i < KI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krs, (__attribute__((address_space(3))) void*)(kstage(kbuf) + (kw * KI + i) * KR * D), 16,
+            k_voff[i], ktile_off, 0, 0);
+#endif
     }
+  };
+  auto vload = [&](int vvb, int rb) {
     if (v_loader) {
+      const int vtile_off = vvb * BLK * D * 2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, (va * CPR + vcc + LT * j) * 16, vtile_off, 0);
-        st.v[4 * j] = y[0]; st.v[4 * j + 1] = y[1]; st.v[4 * j + 2] = y[2]; st.v[4 * j + 3] = y[3];
+        vst[rb][4 * j] = y[0]; vst[rb][4 * j + 1] = y[1]; vst[rb][4 * j + 2] = y[2]; vst[rb][4 * j + 3] = y[3];
       }
     }
   };
-
-  const int k_row0 = k_row_base(ka);
-  auto sstore_k = [&](int kbuf) {
-    if (k_loader) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(&sm.t.k[kbuf][k_row0 + j][8 * kcc]) =
-            make_uint4(st.k[4 * j], st.k[4 * j + 1], st.k[4 * j + 2], st.k[4 * j + 3]);
+  // Before the barrier that publishes a K stage, every wave that issued DMA
+  // into it waits for that DMA.  The DMA is issued ahead of the wave's V loads
+  // of the same step (a scheduling barrier keeps that order) and memory reads
+  // complete in issue order, so vmcnt(4) -- only the four newest V loads may
+  // still be in flight -- covers it.  D = 64 DMA waves issue no V loads and wait
+  // for everything.  (s_waitcnt immediates: vmcnt in bits 3:0, expcnt and
+  // lgkmcnt left at their maxima.)
+  auto wait_kdma = [&] {
+    if constexpr (LT == NT) {
+      __builtin_amdgcn_s_waitcnt(0x0F74);
+    } else {
+      if (k_dma_wave) __builtin_amdgcn_s_waitcnt(0x0F70);
     }
   };
 
   // V^T writes: for each of the thread's 8 dims, the values of its 4 keys as one
   // 8-byte run; two keys per dword assembled with one byte permute.
   const int vpos = vt_pos_base(va);
-  auto sstore_v = [&](int vbuf) {
+  auto sstore_v = [&](int vbuf, int rb) {
     if (v_loader) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w0 = st.v[e >> 1], w1 = st.v[4 + (e >> 1)];
-        const uint32_t w2 = st.v[8 + (e >> 1)], w3 = st.v[12 + (e >> 1)];
+        const uint32_t w0 = vst[rb][e >> 1], w1 = vst[rb][4 + (e >> 1)];
+        const uint32_t w2 = vst[rb][8 + (e >> 1)], w3 = vst[rb][12 + (e >> 1)];
         const int d = 8 * vcc + e;
         const int col = 8 * ((vpos >> 3) ^ vt_swz(d)) + (vpos & 4);
-        *reinterpret_cast<uint2*>(&sm.t.vt[vbuf][d][col]) =
+        *reinterpret_cast<uint2*>(&vts[vbuf][d][col]) =
             make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
       }
     }
   };
-
-  const int p0 = 32 * kh;         // first K row of this wave's key half
 
   // One pipeline step for this wave: online softmax of S (tile vb, already in
   // registers), the QK^T MFMAs of the next tile from K stage kbuf (returned),
@@ -307,7 +329,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     float p[16];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[kbuf][p0 + r32][16 * ks + 8 * g]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kstage(kbuf)) + k_rd[ks]);
       sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sn, 0, 0, 0);
       if (2 * ks < 16) {
         const int i = 2 * ks;
@@ -350,7 +372,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int s0 = 0; s0 < 2; ++s0) {
         const int chunk = (4 * kh + 2 * s0 + g) ^ vt_swz(d);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.vt[vbuf][d][8 * chunk]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vts[vbuf][d][8 * chunk]);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, s0 ? pb1 : pb0, o[db], 0, 0, 0);
       }
     }
@@ -364,7 +386,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.t.k[kbuf][p0 + r32][16 * ks + 8 * g]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kstage(kbuf)) + k_rd[ks]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
     return s;
@@ -402,20 +424,27 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const int n = nlist;
     if (n == 0) continue;
     // Software pipeline with K one tile ahead of V.  At the top of step t the K
-    // stage (t+1)&1 holds K(t+1), the V stage t&1 holds V(t), and S(t) is in
-    // registers.  Step t issues the loads of K(t+2) and V(t+1), runs the QK^T
-    // MFMAs of tile t+1 next to the softmax of tile t (independent work the
-    // scheduler can interleave), then PV of tile t, and stores K(t+2), V(t+1)
-    // into the stages just freed.  Past the end of the list the last tile is
-    // used again (loads stay unconditional; the extra S is discarded).
+    // stage (t+1)&1 holds K(t+1), the V stage t&1 holds V(t), V(t+1) sits in
+    // register buffer (t+1)&1 and S(t) is in registers; the K stage t&1, the V
+    // stage (t+1)&1 and register buffer t&1 were last used in step t-1.  Step t
+    // starts the DMA of K(t+2) into K stage t&1 and the loads of V(t+2) into
+    // register buffer t&1, runs the QK^T MFMAs of tile t+1 next to the softmax
+    // of tile t (independent work the scheduler can interleave), then PV of
+    // tile t, and stores V(t+1) transposed into V stage (t+1)&1.  Each K tile
+    // has one step to arrive and each V tile two.  Past the end of the list the
+    // last tile is used again (loads stay unconditional; the extra S is
+    // discarded).
     auto tile = [&](int t) { return __builtin_amdgcn_readfirstlane(list[min(t, n - 1)]); };
-    gload(tile(0), tile(0));
-    sstore_k(0);
-    sstore_v(0);
+    kdma(tile(0), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    vload(tile(0), 0);
+    vload(tile(1), 1);
+    sstore_v(0, 0);
+    wait_kdma();
     __syncthreads();
-    gload(tile(1), tile(1));
+    kdma(tile(1), 1);
     f32x16 s_cur = qk(0);
-    sstore_k(1);
+    if (k_dma_wave) __builtin_amdgcn_s_waitcnt(0x0F70);   // everything, K(1) included
     __syncthreads();
     // only the last block of the sequence can be ragged, and it is always the
     // last entry of an ascending list
@@ -423,10 +452,12 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     // every LDS address is a per-lane base plus an instruction offset.
     auto body = [&](int t, auto parity) {
       constexpr int P = decltype(parity)::value;   // t & 1
-      gload(tile(t + 2), tile(t + 1));
+      kdma(tile(t + 2), P);
+      __builtin_amdgcn_sched_barrier(0);
+      vload(tile(t + 2), P);
       s_cur = step(s_cur, tile(t), P ^ 1, P, t == n - 1);
-      sstore_k(P);
-      sstore_v(P ^ 1);
+      sstore_v(P ^ 1, P ^ 1);
+      wait_kdma();
       __syncthreads();
     };
     for (int t = 0; t < n; t += 2) {
@@ -436,22 +467,28 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   }
 
   // Merge the two key halves of each query-row half and write the output.
+  // mo[query-row half][accumulator register][lane] overlays the V^T stages
+  // (both 256 * D bytes); mm / ml overlay the block list.
+  static_assert(sizeof(vts) == 2 * (D / 2) * 64 * sizeof(float), "merge overlay size");
+  auto mo = reinterpret_cast<float (*)[D / 2][64]>(&vts[0][0][0]);
+  auto mm = reinterpret_cast<float (*)[32]>(list);
+  auto ml = reinterpret_cast<float (*)[32]>(list) + 2;
   __syncthreads();
   const float l_row = l_part + __shfl_xor(l_part, 32);
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.mg.o[rh][16 * db + i][lane] = o[db][i];
+      for (int i = 0; i < 16; ++i) mo[rh][16 * db + i][lane] = o[db][i];
     if (g == 0) {
-      sm.mg.m[rh][r32] = m_run;
-      sm.mg.l[rh][r32] = l_row;
+      mm[rh][r32] = m_run;
+      ml[rh][r32] = l_row;
     }
   }
   __syncthreads();
   if (kh == 0) {
-    const float m1 = sm.mg.m[rh][r32];
-    const float l1 = sm.mg.l[rh][r32];
+    const float m1 = mm[rh][r32];
+    const float l1 = ml[rh][r32];
     const float mm = fmaxf(m_run, m1);
     float a0 = 0.f, a1 = 0.f;
     if (mm != -INFINITY) {
@@ -471,12 +508,53 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * q4 + r;
-            y[r] = (__bf16)((o[db][i] * a0 + sm.mg.o[rh][16 * db + i][lane] * a1) * inv);
+            y[r] = (__bf16)((o[db][i] * a0 + mo[rh][16 * db + i][lane] * a1) * inv);
           }
           *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * q4 + 4 * g) = y;
         }
     }
   }
+}
+
+// Workgroups the device holds at once for this kernel (CUs x resident
+// workgroups per CU), cached per device.
+template <int D>
+int generation_size() {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<D>, NT, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return 0;
+  cache[dev] = cus * per_cu;
+  return cache[dev];
+}
+
+template <int D>
+int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t* mask,
+                       const int32_t* order, int n_heads, int seq_len, int nb, int W, float c,
+                       u16* O, hipStream_t stream) {
+  // With a work order the rows are launched one device-full of workgroups at a
+  // time.  Every workgroup of a slice starts together, so rows of similar
+  // length from the same head (the planner groups them) walk their ascending
+  // tile lists in step and find each other's K/V tiles in L2; a single launch
+  // lets start times drift apart after the first wave of workgroups retires,
+  // and the tiles in use then spread over the whole head.  Without an order
+  // the grid goes out in one launch.
+  const int total = n_heads * nb;
+  int gen = order ? generation_size<D>() : 0;
+  if (gen <= 0) gen = total;
+  for (int off = 0; off < total; off += gen) {
+    const int count = min(gen, total - off);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)count), dim3(NT), 0, stream, Q, K, V,
+                       mask, order, off, n_heads, seq_len, nb, W, c, O);
+    BSA_CHECK_HIP(hipGetLastError());
+  }
+  return ok();
 }
 
 }  // namespace
@@ -492,15 +570,9 @@ int launch_attn_bf16(const void* q, const void* k, const void* v, const uint64_t
   const u16* K = static_cast<const u16*>(k);
   const u16* V = static_cast<const u16*>(v);
   u16* O = static_cast<u16*>(out);
-  const dim3 grid((unsigned)(n_heads * nb)), block(NT);
   if (head_dim == 128)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, block, 0, stream, Q, K, V, mask, order,
-                       n_heads, seq_len, nb, W, c, O);
-  else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, block, 0, stream, Q, K, V, mask, order,
-                       n_heads, seq_len, nb, W, c, O);
-  BSA_CHECK_HIP(hipGetLastError());
-  return ok();
+    return launch_generations<128>(Q, K, V, mask, order, n_heads, seq_len, nb, W, c, O, stream);
+  return launch_generations<64>(Q, K, V, mask, order, n_heads, seq_len, nb, W, c, O, stream);
 }
 
 }  // namespace bsa

@@ -112,6 +112,9 @@ int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int bl
  * sparse_attn_fwd_planned -- sparse_attn_fwd with a caller-provided work order
  * (any permutation of [0, n_heads * nb), normally from sparse_attn_plan).  Uses no
  * library scratch memory.  Entries outside [0, n_heads * nb) are skipped.
+ * The rows are enqueued as consecutive kernel launches of one device-full of
+ * workgroups each (compute units x resident workgroups per unit), in the order
+ * given, so that the rows of each slice start together.
  */
 int sparse_attn_fwd_planned(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
                             const int32_t* work_order, int n_heads, int seq_len, int head_dim,
