@@ -15,18 +15,16 @@
 //    are lane-local plus one exchange with lane l^32.
 //  * The same 16 probabilities, rounded to bf16, are exactly the B operand of
 //    O^T += V^T P^T, provided the A operand (V^T) pairs each k-slot with the key
-//    the accumulator register held.  Tiles are fetched with a contiguous pattern
-//    (each wave instruction reads 1 KB), which gives every loader thread one
-//    8-dim chunk of keys a, a+16, a+32, a+48.  K rows are placed in LDS in a
-//    permuted key order and V is written transposed (d-major) so that those four
-//    keys form one 8-byte run at positions that line up with four consecutive
-//    MFMA k-slots; every MFMA operand is then a single 16-byte LDS read.  The
-//    transposed V rows have their 16-byte chunks XOR-swizzled (vt_swz) and the
-//    V loader lanes reordered (v_loader_map) so that both the 8-byte writes and
-//    the 16-byte reads are free of LDS bank conflicts.
-//  * Kept K/V tiles stream through a 2-stage LDS ring: the next tile's global
-//    loads are issued before the current tile's math and written to the other
-//    stage after it, with one barrier per tile.
+//    the accumulator register held.  K rows are stored in a permuted key order
+//    (key_of_row) that makes the keys of each group of 8 probability registers
+//    consecutive, so the matching V^T operand is one 16-byte run of a row of
+//    the transposed V tile.  Every MFMA operand is a single 16-byte LDS read.
+//  * V is copied transposed ([head][d][key], rows zero-padded to whole blocks)
+//    by a small kernel ahead of the attention kernel.  K and V^T tiles then both
+//    travel global -> LDS by DMA (buffer_load ... lds), without VGPRs or VALU
+//    work, into 2-stage rings with 16-byte chunks XOR-swizzled against LDS
+//    bank conflicts.  The next tile's DMA is issued before the current tile's
+//    math, with one barrier per tile.
 //  * The row's kept-block list is decoded once per 2048 blocks by wave 0: one mask
 //    word per lane, popcount, and a ballot-based exclusive prefix (one ballot per
 //    bit of the count) give every lane its write offset into an LDS list.
@@ -58,27 +56,23 @@ constexpr float RESCALE_SLACK = 8.0f;
 // 32-bit data format, so the per-access range check against num_records applies.
 constexpr int BUFFER_DWORD3 = 0x00020000;
 
-// Key order inside a tile.  Key a + 16 j (a < 16, j < 4) goes to K row 4a + j
-// and to V^T positions pos0(a) + j with
-// pos0(a) = 32(a>>3) + 16((a>>2)&1) + 8(a&1) + 4((a>>1)&1).  With this pair of
-// maps the k-slot j of the PV operand read at positions 32kh + 16s + 8g .. +7
-// holds the key whose logit sits in accumulator register 8s + j of the QK^T
-// MFMA that read K rows 32kh .. 32kh + 31 (lane group g).
-// (The K row map is simply 4a + j; the inverse gives the key of a row.)
-__device__ __forceinline__ int key_of_row(int r) { return (r >> 2) + 16 * (r & 3); }
-__device__ __forceinline__ int vt_pos_base(int a) {
-  return 32 * (a >> 3) + 16 * ((a >> 2) & 1) + 8 * (a & 1) + 4 * ((a >> 1) & 1);
+// Key order inside a tile.  K row r holds key key_of_row(r): r with bits 2 and
+// 3 exchanged.  The QK^T accumulator register i of lane l (query l % 32) then
+// holds the logit of key 32 kh + 16 (i / 8) + 8 (l / 32) + i % 8, so the eight
+// registers 8 s .. 8 s + 7 that form the bf16 B operand of PV MFMA s cover eight
+// consecutive keys, and the matching A operand is one 16-byte run of a V^T row.
+__device__ __forceinline__ int key_of_row(int r) {
+  return (r & ~12) | ((r >> 1) & 4) | ((r << 1) & 8);
 }
-// LDS bank model behind the V^T layout (measured on gfx950 with the bank-conflict
-// counter): a 16-byte read of a wave is served in four passes over 64 four-byte
-// banks, each pass taking the lanes of one half-wave whose 4-lane quad index has
-// a given bit parity; an 8-byte write is served in passes of 16 consecutive lanes
-// over 32 banks.  V^T rows are 128 bytes, unpadded, and the 16-byte chunk c of
-// row d is stored at chunk c ^ vt_swz(d).  Together with the loader lane maps
-// below, every operand read and every transposing write is conflict free.
-// K rows are D * 2 bytes, unpadded (the tile arrives by LDS DMA, which writes
-// 1 KB runs), and chunk c of row r is stored at chunk c ^ k_swz(r): the rows a
-// read pass touches then land on distinct 16-byte bank groups.
+
+// LDS bank model behind the tile layouts (measured on gfx950 with the
+// bank-conflict counter): a 16-byte read of a wave is served in four passes
+// over 64 four-byte banks, each pass taking the lanes of one half-wave whose
+// 4-lane quad index has a given bit parity.  Both tiles arrive by LDS DMA,
+// which writes 1 KB runs, so rows are unpadded and 16-byte chunks are
+// XOR-swizzled instead: chunk c of K row r sits at chunk c ^ k_swz(r), chunk c
+// of V^T row d at chunk c ^ v_swz(d).  The rows one read pass touches then land
+// on distinct bank groups.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   if constexpr (D == 128)
@@ -86,48 +80,61 @@ __device__ __forceinline__ int k_swz(int r) {
   else
     return (r >> 1) & 7;
 }
-__device__ __forceinline__ int vt_swz(int d) {
-  return (((d >> 1) ^ (d >> 5)) & 1) | (((d >> 4) & 1) << 1) | (((d >> 3) & 1) << 2);
-}
-// V loader lane map: the key group a (a + 16 j are the thread's keys) and the
-// 8-dim chunk vcc each loader thread carries.  Lanes 8i .. 8i+7 read the eight
-// consecutive chunks of one 128-byte line, so a wave still reads 1 KB of
-// consecutive bytes per load instruction; the remaining lane bits are ordered
-// so each 16-lane write pass holds two key groups of different position parity.
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+
+// V transposed in HBM: vt[h][d][key], rows padded to nb * 64 keys with zeros, so
+// a V tile is D runs of 128 bytes and travels by LDS DMA like K.  One workgroup
+// per (head, key block); the tile goes through LDS with a row stride of D + 2
+// elements, which keeps the column reads free of bank conflicts.
 template <int D>
-__device__ __forceinline__ void v_loader_map(int tid, int& a, int& vcc) {
-  const int w = tid >> 6, l = tid & 63;
-  a = (((l >> 3) & 1) << 1) | ((l >> 4) & 1);
-  vcc = l & 7;
-  if constexpr (D == 128) {
-    a += 4 * w;
-    vcc |= ((l >> 5) & 1) << 3;
-  } else {
-    a += 8 * w + (((l >> 5) & 1) << 2);
+__global__ __launch_bounds__(256) void transpose_v_kernel(const u16* __restrict__ V, int N, int nb,
+                                                          u16* __restrict__ VT) {
+  constexpr int S = D + 2;
+  __shared__ __attribute__((aligned(16))) u16 tile[BLK * S];
+  const int t = blockIdx.x % nb, h = blockIdx.x / nb;
+  const u16* src = V + ((size_t)h * N + (size_t)BLK * t) * D;
+  for (int i = threadIdx.x; i < BLK * D / 8; i += 256) {
+    const int r = i / (D / 8), c = i % (D / 8);
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (BLK * t + r < N) x = *reinterpret_cast<const uint4*>(src + (size_t)r * D + 8 * c);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[r * S + 8 * c]);
+    dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+  }
+  __syncthreads();
+  const size_t npad = (size_t)nb * BLK;
+  u16* dst = VT + (size_t)h * D * npad + (size_t)BLK * t;
+  for (int i = threadIdx.x; i < D * 8; i += 256) {
+    const int d = i / 8, c = i % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)tile[(8 * c + 2 * j) * S + d] | ((uint32_t)tile[(8 * c + 2 * j + 1) * S + d] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)d * npad + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int wg_offset,
     int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
   constexpr int CPR = D / 8;             // 16-byte chunks per token row
-  constexpr int KCH = BLK * CPR / NT;    // 16-byte chunks per thread, for K and for V
   constexpr int NDB = D / 32;            // 32-wide output column blocks
   constexpr int NKS = D / 16;            // k-steps of the QK^T contraction
 
-  // LDS.  The two K stages are separate objects so the compiler can tell the
-  // stage being filled by DMA from the stage being read, and waits for a DMA
-  // only where its own stage is read.  After the tile loop the V^T stages hold
-  // the merge of the two key halves' accumulators and the list holds their
-  // running max and sum.
+  // LDS.  Every stage is a separate object so the compiler can tell the stage
+  // being filled by DMA from the stages being read, and waits for a DMA only
+  // where its own stage is read.  After the tile loop the V^T stages hold the
+  // merge of the two key halves' accumulators and the list their running max
+  // and sum.
   __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];   // K stage 0; row r holds key_of_row(r)
   __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];   // K stage 1
-  __shared__ __attribute__((aligned(16))) u16 vts[2][D][BLK];  // V^T stages, chunks swizzled by vt_swz
+  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];   // V^T stage 0; row d holds 64 keys
+  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];   // V^T stage 1
   __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
   __shared__ int nlist;
   auto kstage = [&](int b) { return b ? kst1 : kst0; };
+  auto vstage = [&](int b) { return b ? vts1 : vts0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,7 +154,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   const size_t head_off = (size_t)h * N * D;
   const u16* Qh = Q + head_off;
   const u16* Kh = K + head_off;
-  const u16* Vh = V + head_off;
+  const size_t npad = (size_t)nb * BLK;
+  const u16* VTh = VT + (size_t)h * D * npad;
   const uint64_t* mrow = mask + ((size_t)h * nb + u) * W;
 
   // Q^T fragments (B operand): lane holds Q[row][16ks + 8g .. +7] of its query row.
@@ -177,36 +185,22 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   float m_run = -1.0e30f;
   float l_part = 0.f;
 
-  // Register staging for the V tiles in flight, two deep (vector values, so
-  // they stay in VGPRs): chunk j of this thread in dwords 4j..4j+3.
-  u32x16 vst[2] = {};
-
-  // V loader threads: LT threads, each loading one 8-dim chunk of keys a + 16 j,
-  // j = 0..3, in the lane order of v_loader_map; each wave instruction covers
-  // 1 KB of consecutive bytes.  For d = 128 every thread loads V; for d = 64
-  // the lower half does and the upper half issues the K DMA.
-  constexpr int LT = 16 * CPR;
-  static_assert(LT == NT || 2 * LT == NT, "loader split");
-  const bool v_loader = LT == NT || tid < LT;
-  int va, vcc;
-  v_loader_map<D>(tid, va, vcc);
-
-  // K tiles travel by LDS DMA (global -> LDS without VGPRs).  One wave
-  // instruction writes 1 KB = KR consecutive K rows; lane l fills row
-  // R0 + l / CPR at chunk position l % CPR, so it fetches the key of that row
-  // at the chunk the swizzle stores there.
+  // Both tiles travel by LDS DMA (global -> LDS without VGPRs).  One wave
+  // instruction writes 1 KB: KR consecutive K rows, or 8 consecutive V^T rows.
+  // Lane l fills its row at chunk position l % (chunks per row), so it fetches
+  // the chunk the swizzle stores there.  Each wave issues NI instructions per
+  // tensor and tile.
   constexpr int KR = 1024 / (2 * D);                  // K rows per DMA instruction
-  constexpr int KWAVES = LT == NT ? 4 : 2;            // waves issuing the K DMA
-  constexpr int KI = BLK / (KR * KWAVES);             // DMA instructions per wave
+  constexpr int NI = D / 32;                          // DMA instructions per wave and tensor
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const bool k_dma_wave = LT == NT || wave_u >= 2;
-  const int kw = LT == NT ? wave_u : wave_u - 2;
-  int k_voff[KI];
+  int k_voff[NI], v_voff[NI];
 #pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int r = (kw * KI + i) * KR + lane / CPR;
-    const int c = (lane % CPR) ^ k_swz<D>(r);
-    k_voff[i] = (key_of_row(r) * CPR + c) * 16;
+  for (int i = 0; i < NI; ++i) {
+    const int ii = wave_u * NI + i;
+    const int r = ii * KR + lane / CPR;
+    k_voff[i] = (key_of_row(r) * CPR + ((lane % CPR) ^ k_swz<D>(r))) * 16;
+    const int d = 8 * ii + (lane >> 3);
+    v_voff[i] = d * (int)npad * 2 + 16 * ((lane & 7) ^ v_swz(d));
   }
   // Byte offsets (within a K stage) of this lane's QK^T A operands: row
   // p0 + r32, logical chunk 2 ks + g.
@@ -218,69 +212,32 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     k_rd[ks] = r * D * 2 + 16 * ((2 * ks + g) ^ k_swz<D>(r));
   }
 
-  // Tiles are read with raw buffer loads: one descriptor per head, a scalar
-  // byte offset for the tile and per-thread byte offsets fixed for the whole
-  // row.  The descriptor's range check returns zeros for rows at or past the
-  // sequence end (the ragged last block), which are masked out of the softmax.
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  // Buffer descriptors: one per head and tensor, a scalar byte offset for the
+  // tile and per-lane byte offsets fixed for the whole row.  The range check
+  // returns zeros for K rows past the sequence end (the ragged last block),
+  // which the softmax masks out; V^T rows are zero-padded there.
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)head_bytes, BUFFER_DWORD3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)((uint32_t)N * D * 2u), BUFFER_DWORD3);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Vh), 0, (int)head_bytes, BUFFER_DWORD3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(VTh), 0, (int)(D * npad * 2), BUFFER_DWORD3);
 
   auto kdma = [&](int kvb, int kbuf) {
-    if (k_dma_wave) {
-      const int ktile_off = kvb * BLK * D * 2;
 #ifdef __HIP_DEVICE_COMPILE__   // the host pass cannot form LDS address-space pointers
 #pragma unroll
-      for (int i = 0; i < KI; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            krs, (__attribute__((address_space(3))) void*)(kstage(kbuf) + (kw * KI + i) * KR * D), 16,
-            k_voff[i], ktile_off, 0, 0);
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (__attribute__((address_space(3))) void*)(kstage(kbuf) + (wave_u * NI + i) * KR * D), 16,
+          k_voff[i], kvb * BLK * D * 2, 0, 0);
 #endif
-    }
   };
-  auto vload = [&](int vvb, int rb) {
-    if (v_loader) {
-      const int vtile_off = vvb * BLK * D * 2;
+  auto vdma = [&](int vvb, int vbuf) {
+#ifdef __HIP_DEVICE_COMPILE__
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, (va * CPR + vcc + LT * j) * 16, vtile_off, 0);
-        vst[rb][4 * j] = y[0]; vst[rb][4 * j + 1] = y[1]; vst[rb][4 * j + 2] = y[2]; vst[rb][4 * j + 3] = y[3];
-      }
-    }
-  };
-  // Before the barrier that publishes a K stage, every wave that issued DMA
-  // into it waits for that DMA.  The DMA is issued ahead of the wave's V loads
-  // of the same step (a scheduling barrier keeps that order) and memory reads
-  // complete in issue order, so vmcnt(4) -- only the four newest V loads may
-  // still be in flight -- covers it.  D = 64 DMA waves issue no V loads and wait
-  // for everything.  (s_waitcnt immediates: vmcnt in bits 3:0, expcnt and
-  // lgkmcnt left at their maxima.)
-  auto wait_kdma = [&] {
-    if constexpr (LT == NT) {
-      __builtin_amdgcn_s_waitcnt(0x0F74);
-    } else {
-      if (k_dma_wave) __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-  };
-
-  // V^T writes: for each of the thread's 8 dims, the values of its 4 keys as one
-  // 8-byte run; two keys per dword assembled with one byte permute.
-  const int vpos = vt_pos_base(va);
-  auto sstore_v = [&](int vbuf, int rb) {
-    if (v_loader) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w0 = vst[rb][e >> 1], w1 = vst[rb][4 + (e >> 1)];
-        const uint32_t w2 = vst[rb][8 + (e >> 1)], w3 = vst[rb][12 + (e >> 1)];
-        const int d = 8 * vcc + e;
-        const int col = 8 * ((vpos >> 3) ^ vt_swz(d)) + (vpos & 4);
-        *reinterpret_cast<uint2*>(&vts[vbuf][d][col]) =
-            make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel));
-      }
-    }
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(vstage(vbuf) + (wave_u * NI + i) * 8 * BLK), 16,
+          v_voff[i], vvb * BLK * 2, 0, 0);
+#endif
   };
 
   // One pipeline step for this wave: online softmax of S (tile vb, already in
@@ -289,14 +246,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   // the softmax, so they are issued in the same straight-line block as the
   // exponentials and interleaved with them (one MFMA, then a few VALU ops).
   // s[i] is the logit of query row r32 for the key held by K row
-  // p0 + 8*(i/4) + 4*g + i%4, i.e. key 8kh + 4(i>>3) + 2((i>>2)&1) + g + 16(i&3).
+  // p0 + 8*(i/4) + 4*g + i%4, i.e. key 32kh + 16(i>>3) + 8g + (i&7).
   auto step = [&](f32x16 s, int vb, int kbuf, int vbuf, bool may_be_ragged) {
     if (may_be_ragged) {
       const int hi = N - vb * BLK;   // tile positions >= hi lie past the sequence end
       if (hi < BLK) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = 8 * kh + 4 * (i >> 3) + 2 * ((i >> 2) & 1) + g + 16 * (i & 3);
+          const int key = 32 * kh + 16 * (i >> 3) + 8 * g + (i & 7);
           if (key >= hi) s[i] = -INFINITY;
         }
       }
@@ -371,8 +328,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
       const int d = 32 * db + r32;
 #pragma unroll
       for (int s0 = 0; s0 < 2; ++s0) {
-        const int chunk = (4 * kh + 2 * s0 + g) ^ vt_swz(d);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vts[vbuf][d][8 * chunk]);
+        const int chunk = (4 * kh + 2 * s0 + g) ^ v_swz(d);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vstage(vbuf) + d * BLK + 8 * chunk);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, s0 ? pb1 : pb0, o[db], 0, 0, 0);
       }
     }
@@ -424,27 +381,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const int n = nlist;
     if (n == 0) continue;
     // Software pipeline with K one tile ahead of V.  At the top of step t the K
-    // stage (t+1)&1 holds K(t+1), the V stage t&1 holds V(t), V(t+1) sits in
-    // register buffer (t+1)&1 and S(t) is in registers; the K stage t&1, the V
-    // stage (t+1)&1 and register buffer t&1 were last used in step t-1.  Step t
-    // starts the DMA of K(t+2) into K stage t&1 and the loads of V(t+2) into
-    // register buffer t&1, runs the QK^T MFMAs of tile t+1 next to the softmax
-    // of tile t (independent work the scheduler can interleave), then PV of
-    // tile t, and stores V(t+1) transposed into V stage (t+1)&1.  Each K tile
-    // has one step to arrive and each V tile two.  Past the end of the list the
-    // last tile is used again (loads stay unconditional; the extra S is
-    // discarded).
+    // stage (t+1)&1 holds K(t+1), the V stage t&1 holds V(t) and S(t) is in
+    // registers; the K stage t&1 and the V stage (t+1)&1 were last read in step
+    // t-1.  Step t starts the DMA of K(t+2) and V(t+1) into those two stages,
+    // runs the QK^T MFMAs of tile t+1 next to the softmax of tile t
+    // (independent work the scheduler can interleave), then PV of tile t; the
+    // barrier at its end (whose fence waits for the wave's DMA) publishes both
+    // stages.  Past the end of the list the last tile is used again (loads stay
+    // unconditional; the extra S is discarded).
     auto tile = [&](int t) { return __builtin_amdgcn_readfirstlane(list[min(t, n - 1)]); };
     kdma(tile(0), 0);
-    __builtin_amdgcn_sched_barrier(0);
-    vload(tile(0), 0);
-    vload(tile(1), 1);
-    sstore_v(0, 0);
-    wait_kdma();
+    vdma(tile(0), 0);
     __syncthreads();
     kdma(tile(1), 1);
     f32x16 s_cur = qk(0);
-    if (k_dma_wave) __builtin_amdgcn_s_waitcnt(0x0F70);   // everything, K(1) included
     __syncthreads();
     // only the last block of the sequence can be ragged, and it is always the
     // last entry of an ascending list
@@ -453,11 +403,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     auto body = [&](int t, auto parity) {
       constexpr int P = decltype(parity)::value;   // t & 1
       kdma(tile(t + 2), P);
-      __builtin_amdgcn_sched_barrier(0);
-      vload(tile(t + 2), P);
+      vdma(tile(t + 1), P ^ 1);
       s_cur = step(s_cur, tile(t), P ^ 1, P, t == n - 1);
-      sstore_v(P ^ 1, P ^ 1);
-      wait_kdma();
       __syncthreads();
     };
     for (int t = 0; t < n; t += 2) {
@@ -467,10 +414,10 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   }
 
   // Merge the two key halves of each query-row half and write the output.
-  // mo[query-row half][accumulator register][lane] overlays the V^T stages
-  // (both 256 * D bytes); mm / ml overlay the block list.
-  static_assert(sizeof(vts) == 2 * (D / 2) * 64 * sizeof(float), "merge overlay size");
-  auto mo = reinterpret_cast<float (*)[D / 2][64]>(&vts[0][0][0]);
+  // mo(rh)[accumulator register][lane] overlays V^T stage rh (both 128 * D
+  // bytes); mm / ml overlay the block list.
+  static_assert(sizeof(vts0) == (D / 2) * 64 * sizeof(float), "merge overlay size");
+  auto mo = [&](int half) { return reinterpret_cast<float (*)[64]>(half ? vts1 : vts0); };
   auto mm = reinterpret_cast<float (*)[32]>(list);
   auto ml = reinterpret_cast<float (*)[32]>(list) + 2;
   __syncthreads();
@@ -479,7 +426,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mo[rh][16 * db + i][lane] = o[db][i];
+      for (int i = 0; i < 16; ++i) mo(rh)[16 * db + i][lane] = o[db][i];
     if (g == 0) {
       mm[rh][r32] = m_run;
       ml[rh][r32] = l_row;
@@ -508,7 +455,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * q4 + r;
-            y[r] = (__bf16)((o[db][i] * a0 + mo[rh][16 * db + i][lane] * a1) * inv);
+            y[r] = (__bf16)((o[db][i] * a0 + mo(rh)[16 * db + i][lane] * a1) * inv);
           }
           *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * q4 + 4 * g) = y;
         }
@@ -537,7 +484,10 @@ int generation_size() {
 template <int D>
 int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t* mask,
                        const int32_t* order, int n_heads, int seq_len, int nb, int W, float c,
-                       u16* O, hipStream_t stream) {
+                       u16* O, u16* VT, hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_v_kernel<D>, dim3((unsigned)(n_heads * nb)), dim3(256), 0, stream, V,
+                     seq_len, nb, VT);
+  BSA_CHECK_HIP(hipGetLastError());
   // With a work order the rows are launched one device-full of workgroups at a
   // time.  Every workgroup of a slice starts together, so rows of similar
   // length from the same head (the planner groups them) walk their ascending
@@ -550,7 +500,7 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   if (gen <= 0) gen = total;
   for (int off = 0; off < total; off += gen) {
     const int count = min(gen, total - off);
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)count), dim3(NT), 0, stream, Q, K, V,
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
                        mask, order, off, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());
   }
@@ -559,20 +509,27 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
 
 }  // namespace
 
+size_t vt_bytes(int n_heads, int seq_len, int head_dim) {
+  return (size_t)n_heads * head_dim * n_blocks(seq_len, 64) * 64 * 2;
+}
+
 int launch_attn_bf16(const void* q, const void* k, const void* v, const uint64_t* mask,
                      const int32_t* order, int n_heads, int seq_len, int head_dim, float scale,
-                     void* out, hipStream_t stream) {
+                     void* out, void* vt, hipStream_t stream) {
   const int nb = n_blocks(seq_len, 64);
   const int W = n_words(nb);
   if (nb > 65535) return fail(BSA_ERR_UNSUPPORTED, "at most 65535 key blocks per head (seq_len %d)", seq_len);
+  if ((size_t)head_dim * nb * 64 * 2 > 0x7fffffffull)
+    return fail(BSA_ERR_UNSUPPORTED, "one head's transposed V must stay below 2 GiB (seq_len %d)", seq_len);
   const float c = scale * 1.4426950408889634f;
   const u16* Q = static_cast<const u16*>(q);
   const u16* K = static_cast<const u16*>(k);
   const u16* V = static_cast<const u16*>(v);
   u16* O = static_cast<u16*>(out);
+  u16* VT = static_cast<u16*>(vt);
   if (head_dim == 128)
-    return launch_generations<128>(Q, K, V, mask, order, n_heads, seq_len, nb, W, c, O, stream);
-  return launch_generations<64>(Q, K, V, mask, order, n_heads, seq_len, nb, W, c, O, stream);
+    return launch_generations<128>(Q, K, V, mask, order, n_heads, seq_len, nb, W, c, O, VT, stream);
+  return launch_generations<64>(Q, K, V, mask, order, n_heads, seq_len, nb, W, c, O, VT, stream);
 }
 
 }  // namespace bsa
@@ -587,14 +544,16 @@ extern "C" int sparse_attn_fwd(const void* q, const void* k, const void* v, cons
   const size_t rows = (size_t)n_heads * n_blocks(seq_len, 64);
   const size_t off_tiles = (rows * 4 + 255) & ~size_t(255);
   const size_t off_order = (off_tiles + (size_t)n_heads * 8 + 255) & ~size_t(255);
-  char* ws = static_cast<char*>(scratch(off_order + rows * 4, stream));
+  const size_t off_vt = (off_order + rows * 4 + 255) & ~size_t(255);
+  char* ws = static_cast<char*>(scratch(off_vt + vt_bytes(n_heads, seq_len, head_dim), stream));
   if (!ws) return BSA_ERR_HIP;
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   int64_t* tiles = reinterpret_cast<int64_t*>(ws + off_tiles);
   int32_t* order = reinterpret_cast<int32_t*>(ws + off_order);
   rc = launch_plan(mask_bits, n_heads, seq_len, counts, tiles, order, stream);
   if (rc) return rc;
-  return launch_attn_bf16(q, k, v, mask_bits, order, n_heads, seq_len, head_dim, scale, out, stream);
+  return launch_attn_bf16(q, k, v, mask_bits, order, n_heads, seq_len, head_dim, scale, out,
+                          ws + off_vt, stream);
 }
 
 extern "C" int sparse_attn_fwd_planned(const void* q, const void* k, const void* v,
@@ -607,6 +566,8 @@ extern "C" int sparse_attn_fwd_planned(const void* q, const void* k, const void*
   if (rc) return rc;
   if (!work_order || !aligned(work_order, 4))
     return fail(BSA_ERR_INVALID_ARG, "work_order must be a non-null 4-byte aligned pointer");
+  void* vt = scratch(vt_bytes(n_heads, seq_len, head_dim), stream);
+  if (!vt) return BSA_ERR_HIP;
   return launch_attn_bf16(q, k, v, mask_bits, work_order, n_heads, seq_len, head_dim, scale, out,
-                          stream);
+                          vt, stream);
 }

@@ -35,10 +35,13 @@ int check_attn_args(const void* q, const void* k, const void* v, const void* mas
 int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts, int64_t* head_tiles,
                 int32_t* order, hipStream_t stream);
 
-// Launch the bf16 attention kernel with an optional work order (attn_bf16.hip).
+// Bytes of the transposed-V workspace the bf16 attention path needs.
+size_t vt_bytes(int n_heads, int seq_len, int head_dim);
+// Launch the bf16 attention path (V transpose into `vt`, then the attention
+// kernel) with an optional work order (attn_bf16.hip).
 int launch_attn_bf16(const void* q, const void* k, const void* v, const uint64_t* mask,
                      const int32_t* order, int n_heads, int seq_len, int head_dim, float scale,
-                     void* out, hipStream_t stream);
+                     void* out, void* vt, hipStream_t stream);
 
 }  // namespace bsa
 

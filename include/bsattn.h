@@ -73,10 +73,11 @@ int bsa_mask_words(int seq_len, int block);
  *   out        bf16 [n_heads][seq_len][head_dim], written (round to nearest even).
  *
  * Work is ordered by a device-side planning pass (row popcounts; heads, then rows,
- * in decreasing kept-block count) kept in a library-owned per-device scratch buffer
- * that grows on demand; calls that overlap on one device from different streams
- * race on that buffer -- use sparse_attn_plan + sparse_attn_fwd_planned with
- * caller-owned buffers for concurrent use.
+ * in decreasing kept-block count).  V is first copied transposed ([n_heads][head_dim]
+ * [nb * 64], zero-padded) so its tiles stream like K's.  The plan and the transposed
+ * V live in a library-owned per-device scratch buffer that grows on demand (the
+ * first call at a larger size synchronises the device to grow it); calls that
+ * overlap on one device from different streams race on that buffer.
  */
 int sparse_attn_fwd(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
                     int n_heads, int seq_len, int head_dim, int block_q, int block_k,
@@ -110,11 +111,12 @@ int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int bl
 
 /*
  * sparse_attn_fwd_planned -- sparse_attn_fwd with a caller-provided work order
- * (any permutation of [0, n_heads * nb), normally from sparse_attn_plan).  Uses no
- * library scratch memory.  Entries outside [0, n_heads * nb) are skipped.
- * The rows are enqueued as consecutive kernel launches of one device-full of
- * workgroups each (compute units x resident workgroups per unit), in the order
- * given, so that the rows of each slice start together.
+ * (any permutation of [0, n_heads * nb), normally from sparse_attn_plan).  Entries
+ * outside [0, n_heads * nb) are skipped.  The transposed copy of V uses the
+ * library's per-device scratch buffer (see sparse_attn_fwd about overlapping calls).
+ * After the transpose, the rows are enqueued as consecutive kernel launches of one
+ * device-full of workgroups each (compute units x resident workgroups per unit), in
+ * the order given, so that the rows of each slice start together.
  */
 int sparse_attn_fwd_planned(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
                             const int32_t* work_order, int n_heads, int seq_len, int head_dim,
