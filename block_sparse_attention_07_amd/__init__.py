@@ -6,8 +6,8 @@ computes softmax(scale * Q K^T + M) V where M is 0 on the 64x64 blocks whose bit
 is set in the per-head packed row mask and -inf elsewhere (ScalingAttention,
 section 4.3.2).  Mask producers: ``mask_from_stripes`` (PSA stripe tuples),
 ``block_scores_meanpool`` + ``mask_from_block_scores_topp`` (online top-p with a
-top-k minimum), and ``hilbert3d_order`` + ``permute_tokens`` for Hilbert-ordered
-tokens.  All compute runs in the HIP library ``libbsattn.so``; this package only
+top-k minimum), ``mask_from_threshold_map`` (static masks M = I(T <= p*)), and
+``hilbert3d_order`` + ``permute_tokens`` for Hilbert-ordered tokens.  All compute runs in the HIP library ``libbsattn.so``; this package only
 marshals arguments.
 """
 from .api import (  # noqa: F401
@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     hilbert3d_order,
     mask_from_block_scores_topp,
     mask_from_stripes,
+    mask_from_threshold_map,
     mask_words,
     permute_tokens,
     plan,

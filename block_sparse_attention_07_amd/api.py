@@ -152,6 +152,22 @@ def mask_from_block_scores_topp(scores, p: float, min_blocks: int, out=None):
     return out
 
 
+def mask_from_threshold_map(thresholds, p_head, out=None):
+    """fp32 threshold map [H, nq, nk] and fp32 levels [H] (device) -> int64 mask
+    words [H, nq, ceil(nk/64)] with bit set where T <= p_head[h]."""
+    _dev(thresholds, p_head)
+    _need(thresholds.dtype == torch.float32 and thresholds.dim() == 3, "thresholds must be fp32 [H, nq, nk]")
+    H, nq, nk = thresholds.shape
+    _need(p_head.dtype == torch.float32 and p_head.shape == (H,), "p_head must be fp32 [H]")
+    if out is None:
+        out = torch.empty((H, nq, -(-nk // 64)), dtype=torch.int64, device=thresholds.device)
+    _need(out.shape == (H, nq, -(-nk // 64)) and out.dtype == torch.int64, "bad out")
+    rc = lib().mask_from_threshold_map(_ptr(thresholds), _ptr(p_head), H, nq, nk, _ptr(out),
+                                       _stream(thresholds))
+    check(rc, "mask_from_threshold_map")
+    return out
+
+
 def permute_tokens(x, perm, inverse: bool = False, out=None):
     """Gather (inverse=False) or scatter (inverse=True) token rows of x [H, N, d]."""
     _dev(x, perm)

@@ -32,6 +32,7 @@ SOURCES = [
     "topp.hip",
     "permute.hip",
     "hilbert.hip",
+    "threshold.hip",
 ]
 EXTRA_FLAGS = {"topp.hip": ["-ffp-contract=off"]}
 

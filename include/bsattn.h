@@ -177,6 +177,23 @@ int mask_from_block_scores_topp(const float* scores, int n_heads, int n_q_blocks
                                 float p, int min_blocks, uint64_t* mask_bits, hipStream_t stream);
 
 /*
+ * mask_from_threshold_map -- static block masks from a threshold map
+ * (ScalingAttention section 4.1.2, Eq. 2 and the comparison after it; Appendix A,
+ * Algorithm 1, static block mask generation): mask = I(T <= p*) per head.
+ *
+ *   thresholds  fp32 [n_heads][n_q_blocks][n_k_blocks]: per block, the smallest
+ *               sparsity level at which it is active (device memory, read only).
+ *   p_head      fp32 [n_heads]: each head's level p* (device memory).
+ *   mask_bits   uint64 [n_heads][n_q_blocks][ceil(n_k_blocks/64)], written in full
+ *               (padding bits zero).
+ * The comparison is float32 and inclusive (T == p* keeps the block); NaN entries
+ * are not kept.
+ */
+int mask_from_threshold_map(const float* thresholds, const float* p_head, int n_heads,
+                            int n_q_blocks, int n_k_blocks, uint64_t* mask_bits,
+                            hipStream_t stream);
+
+/*
  * permute_tokens -- token reordering for Hilbert-ordered attention (DFSAttn
  * abstract: tokens reordered along a Hilbert curve before block-sparse attention;
  * SCOPE abstract: attention is then taken over the selected original keys/values,

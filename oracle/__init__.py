@@ -22,4 +22,6 @@ define, in float64 unless the definition fixes another precision:
                       cumulative-mass cut-off) as a fixed float32 procedure.
 * ``hilbert``      -- 3D Hilbert token order (DFSAttn abstract), Skilling's
                       transpose construction.
+* ``threshold``    -- mask instantiation M = I(T <= p*) from a threshold map
+                      (ScalingAttention section 4.1.2, Eq. 2; Algorithm 1).
 """

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert sorted(names) == sorted(_lib.EXPORTS)
 
 
@@ -78,6 +78,9 @@ def test_other_entry_points_validate():
     assert L.permute_tokens(P, P, 1, 10, 8, 2, 0, P, None) == 1             # aliasing
     assert L.sparse_attn_plan(P, 1, 100, 32, P, P, P, None) == 2
     assert L.hilbert3d_order(0, 1, 1, P) == 1
+    assert L.mask_from_threshold_map(None, P, 1, 4, 4, P, None) == 1
+    assert L.mask_from_threshold_map(P, P, 0, 4, 4, P, None) == 1
+    assert L.mask_from_threshold_map(P, ctypes.c_void_p(4098), 1, 4, 4, P, None) == 1
 
 
 def test_hilbert_order_matches_oracle():

@@ -10,7 +10,7 @@ import torch
 
 import block_sparse_attention_07_amd as bsa
 import workloads
-from oracle import block_scores, crm, hilbert, stripes, topp
+from oracle import block_scores, crm, hilbert, stripes, threshold, topp
 from oracle.attention import sparse_attention
 from tests import gpu_util as gu
 
@@ -134,3 +134,37 @@ def test_topp_pipeline_end_to_end():
         rows = perm[u * B:u * B + r.shape[0]]
         g = gu.bf16_host(outh[h][torch.from_numpy(rows.astype(np.int64))])
         gu.assert_bf16_close(g, r, f"topp ({h},{u})")
+
+
+def _threshold_case(T, p):
+    T = np.ascontiguousarray(T, np.float32)
+    p = np.ascontiguousarray(p, np.float32)
+    m = bsa.mask_from_threshold_map(gu.to_dev(T), gu.to_dev(p))
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.mask_host(m), threshold.threshold_mask_bits(T, p))
+
+
+def test_threshold_hand_example_bit_exact():
+    g = json.load(open(os.path.join(GOLD, "threshold_hand_example.json")))
+    T = np.array([[[float(x) for x in row] for row in head] for head in g["T"]], dtype=np.float32)
+    _threshold_case(T, g["p"])
+
+
+@pytest.mark.parametrize("nk", [1, 63, 64, 65, 1182])
+def test_threshold_random_maps_with_ties_bit_exact(nk):
+    rng = np.random.default_rng(100 + nk)
+    H, nq = 3, 37
+    # levels on a coarse grid so exact ties with p* are frequent; a few NaN / inf entries
+    T = (rng.integers(0, 21, size=(H, nq, nk)) / 20.0).astype(np.float32)
+    flat = T.reshape(-1)
+    idx = rng.choice(flat.size, size=min(flat.size, 9), replace=False)
+    flat[idx[:3]] = np.nan
+    flat[idx[3:6]] = np.inf
+    flat[idx[6:]] = -np.inf
+    _threshold_case(T, [0.35, 0.5, 1.0])
+
+
+def test_threshold_workload_map_at_layer_shape():
+    w = workloads.WORKLOADS["wan14b_720p"]
+    T, p = workloads.threshold_map(w.n_heads, w.n_blocks, seed=7)
+    _threshold_case(T, p)

@@ -260,3 +260,21 @@ def random_scores(n_heads: int, nq: int, nk: int, seed: int, spread: float = 3.0
     N(0, spread^2) logits rounded to float32."""
     rng = np.random.default_rng([seed, 3])
     return (rng.standard_normal((n_heads, nq, nk)) * spread).astype(np.float32)
+
+
+def threshold_map(n_heads: int, nb: int, seed: int):
+    """Synthetic threshold maps and per-head levels for mask instantiation tests.
+
+    Stand-in for the calibrated maps of ScalingAttention section 4.1.2 (none can
+    be computed here: they need model weights and prompts).  T grows with the
+    block distance |u - v| (local blocks become active at low levels, as in the
+    pages' Figure 3) plus uniform noise, in [0, 1], float32; levels p*_h ~ U[0.1, 0.6].
+    """
+    rng = np.random.default_rng([seed, 5])
+    u = np.arange(nb)
+    dist = np.abs(u[:, None] - u[None, :]) / max(nb - 1, 1)
+    T = np.empty((n_heads, nb, nb), dtype=np.float32)
+    for h in range(n_heads):
+        T[h] = np.clip(0.6 * dist ** rng.uniform(0.3, 1.0) + 0.4 * rng.random((nb, nb)), 0.0, 1.0)
+    p = rng.uniform(0.1, 0.6, n_heads).astype(np.float32)
+    return T, p
