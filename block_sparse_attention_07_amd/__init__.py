@@ -7,11 +7,14 @@ is set in the per-head packed row mask and -inf elsewhere (ScalingAttention,
 section 4.3.2).  Mask producers: ``mask_from_stripes`` (PSA stripe tuples),
 ``block_scores_meanpool`` + ``mask_from_block_scores_topp`` (online top-p with a
 top-k minimum), ``mask_from_threshold_map`` (static masks M = I(T <= p*)), and
-``hilbert3d_order`` + ``permute_tokens`` for Hilbert-ordered tokens.  All compute runs in the HIP library ``libbsattn.so``; this package only
+``hilbert3d_order`` + ``permute_tokens`` for Hilbert-ordered tokens;
+``attn_fidelity`` measures how far a mask moves attention rows (Hellinger
+distance, ScalingAttention Eqs. 3-4).  All compute runs in the HIP library ``libbsattn.so``; this package only
 marshals arguments.
 """
 from .api import (  # noqa: F401
     BLOCK,
+    attn_fidelity,
     block_scores_meanpool,
     hilbert3d_order,
     mask_from_block_scores_topp,

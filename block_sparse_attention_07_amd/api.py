@@ -168,6 +168,25 @@ def mask_from_threshold_map(thresholds, p_head, out=None):
     return out
 
 
+def attn_fidelity(q, k, mask_bits, rows, scale=None):
+    """Hellinger distance per sampled row fp32 [H, R] and Fidelity Score per head fp32
+    [H] between dense and sparse attention; rows int32 [H, R] token indices (device)."""
+    _dev(q, k, mask_bits, rows)
+    _need(q.dtype == k.dtype == torch.bfloat16 and q.shape == k.shape and q.dim() == 3,
+          "q, k must be bf16 [H, N, d]")
+    H, N, d = q.shape
+    _check_mask(mask_bits, H, N)
+    _need(rows.dtype == torch.int32 and rows.dim() == 2 and rows.shape[0] == H, "rows must be int32 [H, R]")
+    R = rows.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    row_h = torch.empty((H, R), dtype=torch.float32, device=q.device)
+    head_f = torch.empty((H,), dtype=torch.float32, device=q.device)
+    rc = lib().attn_fidelity(_ptr(q), _ptr(k), _ptr(mask_bits), _ptr(rows), H, N, d, BLOCK, R, scale,
+                             _ptr(row_h), _ptr(head_f), _stream(q))
+    check(rc, "attn_fidelity")
+    return row_h, head_f
+
+
 def permute_tokens(x, perm, inverse: bool = False, out=None):
     """Gather (inverse=False) or scatter (inverse=True) token rows of x [H, N, d]."""
     _dev(x, perm)

@@ -33,6 +33,7 @@ SOURCES = [
     "permute.hip",
     "hilbert.hip",
     "threshold.hip",
+    "fidelity.hip",
 ]
 EXTRA_FLAGS = {"topp.hip": ["-ffp-contract=off"]}
 

@@ -1,0 +1,213 @@
+// Hellinger distance / Fidelity Score between dense and sparse attention rows.
+//
+// ScalingAttention section 4.2.1 (Eqs. 3 and 4) and section 4.2.3 (rows drawn
+// by block-wise stratified sampling).  For a sampled query row, P is the dense
+// softmax over every key and P~ the softmax over the keys its mask row keeps.
+// P~ is P restricted to the kept keys and renormalised, so with rho the dense
+// mass on kept keys
+//
+//     H(P, P~)^2 = 1 - sum_j sqrt(p_j p~_j) = 1 - sqrt(rho),
+//     H = sqrt((1 - rho) / (1 + sqrt(rho))),
+//
+// and only two partition sums per row are needed: Z_keep over kept keys and
+// Z_drop over dropped keys, both relative to the row's running maximum; the
+// second form has no cancellation when H is small.  A row that keeps nothing
+// gets H = 1.
+//
+// Pass 1: one workgroup per (1024-key chunk, head, group of 16 sampled rows)
+// computes the fp32 logits of its rows against its keys (bf16 inputs, VALU dot
+// products; the sampled Q rows are broadcast from LDS) and reduces (max,
+// Z_keep, Z_drop) per row.  Pass 2: one workgroup per head merges the chunks,
+// writes each row's H and the head's Fidelity Score 1 - mean H.
+#include <algorithm>
+#include <cmath>
+
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+typedef unsigned short u16;
+constexpr int NT = 256;
+constexpr int RG = 16;          // sampled rows per workgroup
+constexpr int CHUNK = 1024;     // keys per workgroup (16 blocks of 64)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Merge two (max, Z_keep, Z_drop) triples in the exp2 domain.
+__device__ __forceinline__ void merge(float& m, float& zk, float& zd, float m2, float zk2, float zd2) {
+  const float mn = fmaxf(m, m2);
+  const float f1 = m == -INFINITY ? 0.f : exp2f(m - mn);
+  const float f2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mn);
+  zk = zk * f1 + zk2 * f2;
+  zd = zd * f1 + zd2 * f2;
+  m = mn;
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void fidelity_partial_kernel(const u16* __restrict__ Q,
+                                                              const u16* __restrict__ K,
+                                                              const uint64_t* __restrict__ mask,
+                                                              const int32_t* __restrict__ rows, int N,
+                                                              int nb, int W, int n_rows, float c,
+                                                              int n_chunks, float* __restrict__ part) {
+  __shared__ float qs[RG][D];
+  __shared__ uint32_t keepbits[RG];
+  __shared__ float red[NT / 64][RG][3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * RG;
+  const int nr = min(RG, n_rows - r0);
+  const int32_t* hrows = rows + (size_t)h * n_rows + r0;
+
+  for (int i = tid; i < RG * D; i += NT) {
+    const int r = i / D, cc = i % D;
+    float v = 0.f;
+    if (r < nr) {
+      const int tok = hrows[r];
+      if (tok >= 0 && tok < N) v = bf16_to_f32(Q[((size_t)h * N + tok) * D + cc]) * c;
+    }
+    qs[r][cc] = v;
+  }
+  if (tid < RG) {
+    uint32_t bits = 0;
+    if (tid < nr) {
+      const int tok = hrows[tid];
+      if (tok >= 0 && tok < N) {
+        const uint64_t* mrow = mask + ((size_t)h * nb + tok / 64) * W;
+        for (int b = 0; b < CHUNK / 64; ++b) {
+          const int blk = chunk * (CHUNK / 64) + b;
+          if (blk < nb && ((mrow[blk >> 6] >> (blk & 63)) & 1ull)) bits |= 1u << b;
+        }
+      }
+    }
+    keepbits[tid] = bits;
+  }
+  __syncthreads();
+
+  float m[RG], zk[RG], zd[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) { m[r] = -INFINITY; zk[r] = 0.f; zd[r] = 0.f; }
+  const int jend = min(N, (chunk + 1) * CHUNK);
+  for (int j = chunk * CHUNK + tid; j < jend; j += NT) {
+    const u16* kr = K + ((size_t)h * N + j) * D;
+    float acc[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = 0.f;
+#pragma unroll 4
+    for (int c0 = 0; c0 < D; c0 += 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(kr + c0);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kf = bf16_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+#pragma unroll
+        for (int r = 0; r < RG; ++r) acc[r] = fmaf(qs[r][c0 + e], kf, acc[r]);
+      }
+    }
+    const uint32_t b = (uint32_t)((j - chunk * CHUNK) >> 6);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const float s = acc[r];
+      if (s > m[r]) {
+        const float f = m[r] == -INFINITY ? 0.f : exp2f(m[r] - s);
+        zk[r] *= f;
+        zd[r] *= f;
+        m[r] = s;
+      }
+      const float e = exp2f(s - m[r]);
+      if ((keepbits[r] >> b) & 1u) zk[r] += e; else zd[r] += e;
+    }
+  }
+  // Reduce the triples over the workgroup.
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m[r], off), k2 = __shfl_xor(zk[r], off), d2 = __shfl_xor(zd[r], off);
+      merge(m[r], zk[r], zd[r], m2, k2, d2);
+    }
+    if (lane == 0) { red[wave][r][0] = m[r]; red[wave][r][1] = zk[r]; red[wave][r][2] = zd[r]; }
+  }
+  __syncthreads();
+  if (tid < nr) {
+    float mm = red[0][tid][0], kk = red[0][tid][1], dd = red[0][tid][2];
+    for (int wv = 1; wv < NT / 64; ++wv) merge(mm, kk, dd, red[wv][tid][0], red[wv][tid][1], red[wv][tid][2]);
+    float* o = part + (((size_t)h * n_rows + r0 + tid) * n_chunks + chunk) * 3;
+    o[0] = mm; o[1] = kk; o[2] = dd;
+  }
+}
+
+__global__ __launch_bounds__(NT) void fidelity_combine_kernel(const float* __restrict__ part,
+                                                              const int32_t* __restrict__ rows, int N,
+                                                              int n_rows, int n_chunks,
+                                                              float* __restrict__ row_h,
+                                                              float* __restrict__ head_f) {
+  __shared__ float sums[NT];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  float acc = 0.f;
+  for (int r = tid; r < n_rows; r += NT) {
+    const int tok = rows[(size_t)h * n_rows + r];
+    float H = NAN;
+    if (tok >= 0 && tok < N) {
+      const float* p = part + ((size_t)h * n_rows + r) * n_chunks * 3;
+      float m = -INFINITY, zk = 0.f, zd = 0.f;
+      for (int ch = 0; ch < n_chunks; ++ch) merge(m, zk, zd, p[3 * ch], p[3 * ch + 1], p[3 * ch + 2]);
+      if (zk > 0.f) {
+        const float tot = zk + zd;
+        H = sqrtf((zd / tot) / (1.f + sqrtf(zk / tot)));
+      } else {
+        H = 1.f;
+      }
+    }
+    row_h[(size_t)h * n_rows + r] = H;
+    acc += H;
+  }
+  sums[tid] = acc;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (tid < s) sums[tid] += sums[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0 && head_f) head_f[h] = 1.f - sums[0] / (float)n_rows;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" int attn_fidelity(const void* q, const void* k, const uint64_t* mask_bits,
+                             const int32_t* rows, int n_heads, int seq_len, int head_dim, int block,
+                             int n_rows, float scale, float* row_hellinger, float* head_fidelity,
+                             hipStream_t stream) {
+  using namespace bsa;
+  if (!q || !k || !mask_bits || !rows || !row_hellinger)
+    return fail(BSA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(mask_bits, 8) || !aligned(rows, 4) ||
+      !aligned(row_hellinger, 4) || (head_fidelity && !aligned(head_fidelity, 4)))
+    return fail(BSA_ERR_INVALID_ARG, "misaligned pointer argument");
+  if (n_heads < 1 || seq_len < 1 || n_rows < 1) return fail(BSA_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(BSA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (block != 64) return fail(BSA_ERR_UNSUPPORTED, "only 64-token blocks are implemented");
+  if (head_dim != 64 && head_dim != 128) return fail(BSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (n_heads > 65535 || (n_rows + RG - 1) / RG > 65535)
+    return fail(BSA_ERR_UNSUPPORTED, "at most 65535 heads and 65535 * 16 rows per call");
+  const int nb = n_blocks(seq_len, 64);
+  const int W = n_words(nb);
+  const int n_chunks = (seq_len + CHUNK - 1) / CHUNK;
+  float* part = static_cast<float*>(scratch((size_t)n_heads * n_rows * n_chunks * 3 * sizeof(float), stream));
+  if (!part) return BSA_ERR_HIP;
+  const float c = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)n_chunks, (unsigned)n_heads, (unsigned)((n_rows + RG - 1) / RG));
+  const u16* Q = static_cast<const u16*>(q);
+  const u16* K = static_cast<const u16*>(k);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(fidelity_partial_kernel<128>, grid, dim3(NT), 0, stream, Q, K, mask_bits, rows,
+                       seq_len, nb, W, n_rows, c, n_chunks, part);
+  else
+    hipLaunchKernelGGL(fidelity_partial_kernel<64>, grid, dim3(NT), 0, stream, Q, K, mask_bits, rows,
+                       seq_len, nb, W, n_rows, c, n_chunks, part);
+  BSA_CHECK_HIP(hipGetLastError());
+  hipLaunchKernelGGL(fidelity_combine_kernel, dim3((unsigned)n_heads), dim3(NT), 0, stream, part, rows,
+                     seq_len, n_rows, n_chunks, row_hellinger, head_fidelity);
+  BSA_CHECK_HIP(hipGetLastError());
+  return ok();
+}

@@ -194,6 +194,28 @@ int mask_from_threshold_map(const float* thresholds, const float* p_head, int n_
                             hipStream_t stream);
 
 /*
+ * attn_fidelity -- Hellinger distance and Fidelity Score between dense and sparse
+ * attention on sampled query rows (ScalingAttention section 4.2.1, Eqs. 3 and 4;
+ * rows drawn by block-wise stratified sampling, section 4.2.3).  For row i of head
+ * h, P = softmax(scale * q_i K^T) over every key and P~ = the softmax over the keys
+ * of the blocks its mask row keeps; H = (1/sqrt 2) * ||sqrt P - sqrt P~||_2.
+ * Computed through the equivalent form H = sqrt((1 - rho) / (1 + sqrt rho)), rho =
+ * the dense mass on kept keys, with fp32 logits from the bf16 inputs.
+ *
+ *   q, k           bf16 [n_heads][seq_len][head_dim], head_dim in {64, 128}; block 64.
+ *   mask_bits      uint64 [n_heads][nb][W] as for sparse_attn_fwd.
+ *   rows           int32 [n_heads][n_rows]: token index of each sampled query row
+ *                  (device memory); an index outside [0, seq_len) yields NaN.
+ *   row_hellinger  fp32 [n_heads][n_rows], written; 1 for a row that keeps nothing.
+ *   head_fidelity  fp32 [n_heads] or NULL: 1 - mean of the head's row distances.
+ * Uses the library's per-device scratch buffer for per-chunk partial sums (see
+ * sparse_attn_fwd about overlapping calls).
+ */
+int attn_fidelity(const void* q, const void* k, const uint64_t* mask_bits, const int32_t* rows,
+                  int n_heads, int seq_len, int head_dim, int block, int n_rows, float scale,
+                  float* row_hellinger, float* head_fidelity, hipStream_t stream);
+
+/*
  * permute_tokens -- token reordering for Hilbert-ordered attention (DFSAttn
  * abstract: tokens reordered along a Hilbert curve before block-sparse attention;
  * SCOPE abstract: attention is then taken over the selected original keys/values,

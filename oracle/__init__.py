@@ -24,4 +24,7 @@ define, in float64 unless the definition fixes another precision:
                       transpose construction.
 * ``threshold``    -- mask instantiation M = I(T <= p*) from a threshold map
                       (ScalingAttention section 4.1.2, Eq. 2; Algorithm 1).
+* ``fidelity``     -- Hellinger distance / Fidelity Score between dense and
+                      sparse attention rows (ScalingAttention Eqs. 3-4,
+                      section 4.2.3 stratified rows).
 """

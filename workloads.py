@@ -278,3 +278,17 @@ def threshold_map(n_heads: int, nb: int, seed: int):
         T[h] = np.clip(0.6 * dist ** rng.uniform(0.3, 1.0) + 0.4 * rng.random((nb, nb)), 0.0, 1.0)
     p = rng.uniform(0.1, 0.6, n_heads).astype(np.float32)
     return T, p
+
+
+def stratified_rows(n_heads: int, n_tokens: int, n_rows: int, seed: int) -> np.ndarray:
+    """Block-wise stratified row sample (ScalingAttention section 4.2.3): the
+    token rows are cut into n_rows equal strata and one row is drawn uniformly
+    from each, independently per head.  int32 [n_heads, n_rows]."""
+    rng = np.random.default_rng([seed, 6])
+    edges = (np.arange(n_rows + 1) * n_tokens) // n_rows
+    out = np.empty((n_heads, n_rows), np.int32)
+    for h in range(n_heads):
+        for r in range(n_rows):
+            lo, hi = edges[r], max(edges[r + 1], edges[r] + 1)
+            out[h, r] = min(int(rng.integers(lo, hi)), n_tokens - 1)
+    return out
