@@ -6,7 +6,8 @@ computes softmax(scale * Q K^T + M) V where M is 0 on the 64x64 blocks whose bit
 is set in the per-head packed row mask and -inf elsewhere (ScalingAttention,
 section 4.3.2).  Mask producers: ``mask_from_stripes`` (PSA stripe tuples),
 ``block_scores_meanpool`` + ``mask_from_block_scores_topp`` (online top-p with a
-top-k minimum), ``mask_from_threshold_map`` (static masks M = I(T <= p*)), and
+top-k minimum), ``mask_from_threshold_map`` (static masks M = I(T <= p*)) with
+``threshold_map_resize`` / ``mask_resize`` for other resolutions, and
 ``hilbert3d_order`` + ``permute_tokens`` for Hilbert-ordered tokens;
 ``attn_fidelity`` measures how far a mask moves attention rows (Hellinger
 distance, ScalingAttention Eqs. 3-4).  All compute runs in the HIP library ``libbsattn.so``; this package only
@@ -20,9 +21,11 @@ from .api import (  # noqa: F401
     mask_from_block_scores_topp,
     mask_from_stripes,
     mask_from_threshold_map,
+    mask_resize,
     mask_words,
     permute_tokens,
     plan,
     sparse_attn,
+    threshold_map_resize,
 )
 from ._lib import BsaError, LIB_PATH  # noqa: F401

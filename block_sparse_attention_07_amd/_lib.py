@@ -26,6 +26,8 @@ SIGNATURES = {
     "block_scores_meanpool": [_p, _p, _i, _i, _i, _i, _f, _p, _p],
     "mask_from_block_scores_topp": [_p, _i, _i, _i, _f, _i, _p, _p],
     "mask_from_threshold_map": [_p, _p, _i, _i, _i, _p, _p],
+    "mask_resize": [_p, _i, _i, _i, _p, _p],
+    "threshold_map_resize": [_p, _i, _i, _i, _p, _p],
     "attn_fidelity": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p],
     "permute_tokens": [_p, _p, _i, _i, _i, _i, _i, _p, _p],
     "hilbert3d_order": [_i, _i, _i, _p],

@@ -168,6 +168,36 @@ def mask_from_threshold_map(thresholds, p_head, out=None):
     return out
 
 
+def mask_resize(mask_bits, nb_base: int, nb_target: int, out=None):
+    """Region maps int64 [H, nb_base, ceil(nb_base/64)] -> [H, nb_target, ceil(nb_target/64)]
+    (Eq. 7: bilinear interpolation with a ceiling)."""
+    _dev(mask_bits)
+    H = mask_bits.shape[0]
+    _need(mask_bits.dtype == torch.int64 and mask_bits.shape == (H, nb_base, -(-nb_base // 64)),
+          "mask_bits must be int64 [H, nb_base, ceil(nb_base/64)]")
+    if out is None:
+        out = torch.empty((H, nb_target, -(-nb_target // 64)), dtype=torch.int64, device=mask_bits.device)
+    _need(out.shape == (H, nb_target, -(-nb_target // 64)) and out.dtype == torch.int64, "bad out")
+    rc = lib().mask_resize(_ptr(mask_bits), H, int(nb_base), int(nb_target), _ptr(out), _stream(mask_bits))
+    check(rc, "mask_resize")
+    return out
+
+
+def threshold_map_resize(thresholds, nb_target: int, out=None):
+    """Threshold maps fp32 [H, nb, nb] -> [H, nb_target, nb_target] (min over the
+    positive-weight bilinear samples)."""
+    _dev(thresholds)
+    _need(thresholds.dtype == torch.float32 and thresholds.dim() == 3 and
+          thresholds.shape[1] == thresholds.shape[2], "thresholds must be fp32 [H, nb, nb]")
+    H, nb, _ = thresholds.shape
+    if out is None:
+        out = torch.empty((H, nb_target, nb_target), dtype=torch.float32, device=thresholds.device)
+    _need(out.shape == (H, nb_target, nb_target) and out.dtype == torch.float32, "bad out")
+    rc = lib().threshold_map_resize(_ptr(thresholds), H, nb, int(nb_target), _ptr(out), _stream(thresholds))
+    check(rc, "threshold_map_resize")
+    return out
+
+
 def attn_fidelity(q, k, mask_bits, rows, scale=None):
     """Hellinger distance per sampled row fp32 [H, R] and Fidelity Score per head fp32
     [H] between dense and sparse attention; rows int32 [H, R] token indices (device)."""

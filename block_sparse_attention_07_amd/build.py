@@ -34,6 +34,7 @@ SOURCES = [
     "hilbert.hip",
     "threshold.hip",
     "fidelity.hip",
+    "resize.hip",
 ]
 EXTRA_FLAGS = {"topp.hip": ["-ffp-contract=off"]}
 

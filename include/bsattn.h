@@ -194,6 +194,30 @@ int mask_from_threshold_map(const float* thresholds, const float* p_head, int n_
                             hipStream_t stream);
 
 /*
+ * mask_resize -- resolution scaling of packed region maps (ScalingAttention section
+ * 4.3.1, Eq. 7: bilinear interpolation at (u / s, v / s), s = nb_target / nb_base,
+ * then a ceiling, so any overlap with an active region is kept).  On a binary map
+ * this is exact in integers: target block (u, v) is kept iff a base sample with
+ * positive bilinear weight is kept (samples at integer coordinates, clamped at the
+ * last one).
+ *   base_bits    uint64 [n_heads][nb_base][ceil(nb_base/64)], read only.
+ *   target_bits  uint64 [n_heads][nb_target][ceil(nb_target/64)], written in full.
+ */
+int mask_resize(const uint64_t* base_bits, int n_heads, int nb_base, int nb_target,
+                uint64_t* target_bits, hipStream_t stream);
+
+/*
+ * threshold_map_resize -- the threshold-map counterpart of mask_resize: each target
+ * entry is the minimum of the base entries with positive bilinear weight (NaN
+ * ignored), so I(resized T <= p) equals mask_resize of I(T <= p) for every p (a
+ * ceiling on thresholds would drop activity instead of keeping it).
+ *   base    fp32 [n_heads][nb_base][nb_base], read only.
+ *   target  fp32 [n_heads][nb_target][nb_target], written; must not alias base.
+ */
+int threshold_map_resize(const float* base, int n_heads, int nb_base, int nb_target, float* target,
+                         hipStream_t stream);
+
+/*
  * attn_fidelity -- Hellinger distance and Fidelity Score between dense and sparse
  * attention on sampled query rows (ScalingAttention section 4.2.1, Eqs. 3 and 4;
  * rows drawn by block-wise stratified sampling, section 4.2.3).  For row i of head

@@ -27,4 +27,6 @@ define, in float64 unless the definition fixes another precision:
 * ``fidelity``     -- Hellinger distance / Fidelity Score between dense and
                       sparse attention rows (ScalingAttention Eqs. 3-4,
                       section 4.2.3 stratified rows).
+* ``resize``       -- resolution scaling of region / threshold maps
+                      (ScalingAttention section 4.3.1, Eq. 7).
 """

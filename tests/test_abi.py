@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     assert sorted(names) == sorted(_lib.EXPORTS)
 
 
@@ -81,6 +81,10 @@ def test_other_entry_points_validate():
     assert L.mask_from_threshold_map(None, P, 1, 4, 4, P, None) == 1
     assert L.mask_from_threshold_map(P, P, 0, 4, 4, P, None) == 1
     assert L.mask_from_threshold_map(P, ctypes.c_void_p(4098), 1, 4, 4, P, None) == 1
+    assert L.mask_resize(None, 1, 4, 8, P, None) == 1
+    assert L.mask_resize(P, 1, 0, 8, P, None) == 1
+    assert L.threshold_map_resize(P, 1, 4, 8, P, None) == 1                # aliasing
+    assert L.threshold_map_resize(P, 1, 4, 8, ctypes.c_void_p(8194), None) == 1
     f = ctypes.c_float
     assert L.attn_fidelity(None, P, P, P, 1, 100, 128, 64, 16, f(0.1), P, None, None) == 1
     assert L.attn_fidelity(P, P, P, P, 1, 100, 96, 64, 16, f(0.1), P, None, None) == 2

@@ -10,7 +10,7 @@ import torch
 
 import block_sparse_attention_07_amd as bsa
 import workloads
-from oracle import block_scores, crm, hilbert, stripes, threshold, topp
+from oracle import block_scores, crm, hilbert, resize, stripes, threshold, topp
 from oracle.attention import sparse_attention
 from tests import gpu_util as gu
 
@@ -168,3 +168,30 @@ def test_threshold_workload_map_at_layer_shape():
     w = workloads.WORKLOADS["wan14b_720p"]
     T, p = workloads.threshold_map(w.n_heads, w.n_blocks, seed=7)
     _threshold_case(T, p)
+
+
+@pytest.mark.parametrize("nb,nt", [(6, 12), (9, 9), (20, 13), (70, 131), (100, 64), (33, 200)])
+def test_resize_maps_match_oracle(nb, nt):
+    rng = np.random.default_rng(nb * 1000 + nt)
+    H = 2
+    keep = rng.random((H, nb, nb)) < 0.15
+    got = bsa.mask_resize(gu.to_dev(crm.pack_rows(keep)), nb, nt)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.mask_host(got), crm.pack_rows(resize.resize_region(keep, nt)))
+    T = rng.random((H, nb, nb), dtype=np.float32)
+    T[0, 0, nb - 1] = np.nan
+    Tt = bsa.threshold_map_resize(gu.to_dev(T), nt).cpu().numpy()
+    ref = resize.resize_threshold(T, nt)
+    assert np.array_equal(np.isnan(Tt), np.isnan(ref))
+    assert np.array_equal(Tt[~np.isnan(Tt)], ref[~np.isnan(ref)])
+
+
+def test_resize_commutes_with_threshold_masks_on_device():
+    """Resizing the threshold map then instantiating equals instantiating then resizing
+    the region map (the conservative reading of Eq. 7), at the 480p -> 720p block counts."""
+    T, p = workloads.threshold_map(4, 512, seed=8)
+    Td, pd = gu.to_dev(T), gu.to_dev(p)
+    a = bsa.mask_from_threshold_map(bsa.threshold_map_resize(Td, 1182), pd)
+    b = bsa.mask_resize(bsa.mask_from_threshold_map(Td, pd), 512, 1182)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
