@@ -1,6 +1,7 @@
 """Benchmark: block-sparse attention at the Wan2.1-14B 720p layer shape on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
+                    [--sweep] [--aux]
 
 Workload (synthetic, seeded): 40 heads, head_dim 128, bf16, latent grid
 21x45x80 = 75,600 tokens (1182 blocks of 64); 8 heads keep every block, the
@@ -17,6 +18,11 @@ Reported on one JSON line:
   roofline   the attention kernel alone (planned entry, events on its stream):
              algorithmic flops per launch / average launch time vs the bf16 MFMA peak
   cpu_baseline  the float64 CPU oracle on a bounded sample of query blocks
+
+--sweep  (extra, to stderr) uniform random masks at 5 .. 100 % density on the same
+         shape: speedup against 1/density (the analogue of ScalingAttention Fig. 5).
+--aux    (extra, to stderr) the HBM-bound kernels of the path (mask producers,
+         block scores, top-p, permutation, resize, fidelity) in GB/s vs 8 TB/s.
 """
 from __future__ import annotations
 
@@ -98,6 +104,78 @@ def cpu_baseline(w, q, k, v, bits, keep, budget_s=12.0):
     }
 
 
+def device_uniform_mask(torch, H, nb, density, seed, dev):
+    """Bernoulli(density) blocks drawn on the device (seeded), packed to int64 words."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    keep = torch.rand((H, nb, nb), generator=g, device=dev) < density
+    W = -(-nb // 64)
+    pad = torch.zeros((H, nb, W * 64), dtype=torch.int64, device=dev)
+    pad[..., :nb] = keep.to(torch.int64)
+    shifts = torch.arange(64, device=dev, dtype=torch.int64)
+    words = (pad.view(H, nb, W, 64) << shifts).sum(-1)      # distinct bits: the sum is the OR
+    return words, int(keep.sum().item())
+
+
+def density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
+    dev = qd.device
+    for dens in (0.05, 0.10, 0.20, 0.40, 0.60, 0.80, 1.00):
+        md, kept = device_uniform_mask(torch, w.n_heads, w.n_blocks, dens, 100 + int(dens * 100), dev)
+        f = lambda: bsa.sparse_attn(qd, kd, vd, md, w.scale, out=out)
+        f()
+        ms = timed(f, 5)
+        rec = {"sweep_density": dens, "kept_tiles": kept, "ms": round(ms, 3),
+               "tflops": round(kept * tile_flops(w.head_dim) / (ms * 1e-3) / 1e12, 1),
+               "speedup_vs_full": round(ms_full / ms, 3), "ideal_speedup": round(1 / dens, 3)}
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+        del md
+
+
+def aux_kernels(bsa, torch, timed):
+    """Effective bandwidth of the HBM-bound kernels on the configs' shapes."""
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    H, N, d = 40, 75600, 128
+    nb = -(-N // 64)
+    W = -(-nb // 64)
+    x = torch.randn((H, N, d), generator=g, device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+
+    def report(name, fn, nbytes, n=5):
+        fn()
+        ms = timed(fn, n)
+        print(json.dumps({"aux": name, "ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "frac_of_8TBps": round(nbytes / (ms * 1e-3) / 8e12, 3)}), file=sys.stderr, flush=True)
+
+    perm = torch.randperm(N, generator=g, device=dev).to(torch.int32)
+    report("permute_tokens gather [40,75600,128] bf16", lambda: bsa.permute_tokens(x, perm, out=y), 2 * x.numel() * 2)
+    scores = torch.empty((H, nb, nb), dtype=torch.float32, device=dev)
+    report("block_scores_meanpool q,k [40,75600,128]", lambda: bsa.block_scores_meanpool(x, x, out=scores),
+           2 * x.numel() * 2 + scores.numel() * 4)
+    scores.normal_(generator=g)
+    mw = torch.empty((H, nb, W), dtype=torch.int64, device=dev)
+    report("mask_from_block_scores_topp p=0.9 min 8", lambda: bsa.mask_from_block_scores_topp(scores, 0.9, 8, out=mw),
+           scores.numel() * 4 + mw.numel() * 8)
+    pth = torch.rand((H,), generator=g, device=dev)
+    report("mask_from_threshold_map [40,1182,1182]", lambda: bsa.mask_from_threshold_map(scores, pth, out=mw),
+           scores.numel() * 4 + mw.numel() * 8)
+    tb = torch.rand((H, 512, 512), generator=g, device=dev)
+    tt = torch.empty((H, nb, nb), dtype=torch.float32, device=dev)
+    report("threshold_map_resize 512 -> 1182", lambda: bsa.threshold_map_resize(tb, nb, out=tt),
+           tb.numel() * 4 + tt.numel() * 4)
+    mb = torch.zeros((H, 512, 8), dtype=torch.int64, device=dev)
+    report("mask_resize 512 -> 1182", lambda: bsa.mask_resize(mb, 512, nb, out=mw), mb.numel() * 8 + mw.numel() * 8)
+    rows = torch.randint(0, N, (H, 16), generator=g, device=dev, dtype=torch.int32)
+    report("attn_fidelity 16 rows per head", lambda: bsa.attn_fidelity(x, x, mw, rows), x.numel() * 2)
+    Hh, T, F = 24, 33, 3840
+    nbh = T * F // 64
+    params = torch.tensor([[0, 5, 0, 0, 3, 0, 3]] * Hh, dtype=torch.int32, device=dev)
+    ms_out = torch.empty((Hh, nbh, -(-nbh // 64)), dtype=torch.int64, device=dev)
+    report("mask_from_stripes HunyuanVideo 24 heads", lambda: bsa.mask_from_stripes(params, T, F, T * F, out=ms_out),
+           ms_out.numel() * 8)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +184,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for counter collection: a few planned launches plus a 1 GiB copy")
+    ap.add_argument("--sweep", action="store_true", help="also run the density sweep (stderr)")
+    ap.add_argument("--aux", action="store_true", help="also time the HBM-bound kernels (stderr)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -207,6 +287,10 @@ def main():
             "kernel_ms": round(ms_k, 4),
         },
     }
+    if args.sweep:
+        density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
+    if args.aux:
+        aux_kernels(bsa, torch, timed)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, bits, keep)
     else:

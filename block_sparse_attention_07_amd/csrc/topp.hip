@@ -11,9 +11,10 @@
 // own (Cody-Waite reduction with a two-part ln 2, degree-7 Taylor polynomial in
 // Horner form, 2^n assembled from exponent bits, 0 below -87).
 //
-// One workgroup per score row: the row is staged in LDS, bitonic-sorted by
-// (score descending, index ascending), the exponentials are summed and scanned
-// by one lane in sorted order, and the chosen blocks are OR-ed into LDS words.
+// One workgroup per score row: the row is held in registers (E values per lane),
+// bitonic-sorted by (score descending, index ascending) mostly inside threads and
+// waves, the exponentials are summed and scanned by one lane in sorted order,
+// and the chosen blocks are OR-ed into LDS words.
 #include <cmath>
 
 #include "bsa_internal.h"
@@ -59,13 +60,78 @@ __device__ __forceinline__ bool before(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// Bitonic sort of npad = E * NT (key, index) pairs into "before" order, with
+// thread t holding positions E t .. E t + E - 1 in registers.  Partners closer
+// than E positions are exchanged inside the thread, partners within the wave by
+// lane shuffles, and only the few stages whose partner lies in another wave go
+// through LDS (lk / li, with barriers).
+template <int E>
+__device__ void bitonic_sort(float (&k)[E], int (&ix)[E], float* lk, unsigned short* li, int tid) {
+  constexpr int npad = E * NT;
+  for (int size = 2; size <= npad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int f = e ^ stride;
+          if (f > e) {
+            const bool up = ((E * tid + e) & size) == 0;
+            const bool sw = up ? before(k[f], ix[f], k[e], ix[e]) : before(k[e], ix[e], k[f], ix[f]);
+            if (sw) {
+              const float tk = k[e]; k[e] = k[f]; k[f] = tk;
+              const int ti = ix[e]; ix[e] = ix[f]; ix[f] = ti;
+            }
+          }
+        }
+      } else {
+        float pk[E];
+        int pi[E];
+        if (stride < E * 64) {
+          const int ld = stride / E;                 // lane distance inside the wave
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            pk[e] = __shfl_xor(k[e], ld);
+            pi[e] = __shfl_xor(ix[e], ld);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            lk[E * tid + e] = k[e];
+            li[E * tid + e] = (unsigned short)ix[e];
+          }
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            pk[e] = lk[(E * tid + e) ^ stride];
+            pi[e] = li[(E * tid + e) ^ stride];
+          }
+          __syncthreads();
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int pos = E * tid + e;
+          const bool lower = (pos & stride) == 0, up = (pos & size) == 0;
+          const bool mine_first = before(k[e], ix[e], pk[e], pi[e]);
+          const bool keep_mine = (lower == up) ? mine_first : !mine_first;
+          if (!keep_mine) {
+            k[e] = pk[e];
+            ix[e] = pi[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int E>
 __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scores, int nk, int W,
                                                   float p, int min_blocks,
                                                   uint64_t* __restrict__ mask) {
 #pragma clang fp contract(off)
-  __shared__ float key[MAX_N];
-  __shared__ unsigned short idx[MAX_N];
-  __shared__ float ex[MAX_N];
+  constexpr int npad = E * NT;
+  __shared__ __attribute__((aligned(16))) float key[npad];
+  __shared__ unsigned short idx[npad];
+  __shared__ float ex[npad];
   __shared__ float red[NT];
   __shared__ unsigned long long words[MAX_N / 64];
   __shared__ int k_keep;
@@ -73,19 +139,20 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
   const int tid = threadIdx.x;
   const size_t row = blockIdx.x;
   const float* s = scores + row * (size_t)nk;
-  int npad = 1;
-  while (npad < nk) npad <<= 1;
 
+  float k[E];
+  int ix[E];
   float mx = -INFINITY;
-  for (int j = tid; j < npad; j += NT) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = E * tid + e;
     if (j < nk) {
-      const float v = s[j];
-      key[j] = v;
-      idx[j] = (unsigned short)j;
-      mx = fmaxf(mx, v);
+      k[e] = s[j];
+      ix[e] = j;
+      mx = fmaxf(mx, k[e]);
     } else {
-      key[j] = -INFINITY;
-      idx[j] = 0xffff;
+      k[e] = -INFINITY;
+      ix[e] = 0xffff;
     }
   }
   red[tid] = mx;
@@ -96,35 +163,33 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
     __syncthreads();
   }
   const float m = red[0];
-  for (int j = tid; j < nk; j += NT) ex[j] = exp_cw(key[j] - m);
-  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (E * tid + e < nk) ex[E * tid + e] = exp_cw(k[e] - m);
 
-  // bitonic sort of (key, idx) into "before" order
-  for (int size = 2; size <= npad; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < npad; i += NT) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;
-          const float ki = key[i], kj = key[j];
-          const int ii = idx[i], ij = idx[j];
-          const bool swap = up ? before(kj, ij, ki, ii) : before(ki, ii, kj, ij);
-          if (swap) {
-            key[i] = kj; key[j] = ki;
-            idx[i] = (unsigned short)ij; idx[j] = (unsigned short)ii;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  bitonic_sort<E>(k, ix, key, idx, tid);
+  __syncthreads();                       // ex[] complete, LDS exchange buffers free
+
+  // exponentials in sorted order
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int r = E * tid + e;
+    idx[r] = (unsigned short)ix[e];
+    if (r < nk) key[r] = ex[ix[e]];
   }
-
-  // exponentials in sorted order (reuse key[])
-  for (int r = tid; r < nk; r += NT) key[r] = ex[idx[r]];
   __syncthreads();
+  // The two sums are sequential by definition; one lane runs each, reading four
+  // values per LDS load so the loads run ahead of the dependent adds.
+  const float4* key4 = reinterpret_cast<const float4*>(key);
   if (tid == 0) {
     float z = 0.0f;
-    for (int r = 0; r < nk; ++r) z = z + key[r];
+    int r = 0;
+#pragma unroll 4
+    for (; r + 4 <= nk; r += 4) {
+      const float4 v = key4[r >> 2];
+      z = z + v.x; z = z + v.y; z = z + v.z; z = z + v.w;
+    }
+    for (; r < nk; ++r) z = z + key[r];
     red[0] = z;
   }
   __syncthreads();
@@ -134,12 +199,19 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
   if (tid == 0) {
     float c = 0.0f;
     int kp = nk;
-    for (int r = 0; r < nk; ++r) {
+    int r = 0;
+    // kp keeps the first crossing; the loop stops at the end of the group of
+    // four where it happens
+    for (; r + 4 <= nk && kp == nk; r += 4) {
+      const float4 v = key4[r >> 2];
+      c = c + v.x; kp = (kp == nk && c >= p) ? r + 1 : kp;
+      c = c + v.y; kp = (kp == nk && c >= p) ? r + 2 : kp;
+      c = c + v.z; kp = (kp == nk && c >= p) ? r + 3 : kp;
+      c = c + v.w; kp = (kp == nk && c >= p) ? r + 4 : kp;
+    }
+    for (; r < nk && kp == nk; ++r) {
       c = c + key[r];
-      if (c >= p) {
-        kp = r + 1;
-        break;
-      }
+      if (c >= p) kp = r + 1;
     }
     const int floor_k = min_blocks < nk ? min_blocks : nk;
     k_keep = kp > floor_k ? kp : floor_k;
@@ -173,8 +245,18 @@ extern "C" int mask_from_block_scores_topp(const float* scores, int n_heads, int
   if (min_blocks < 0) return fail(BSA_ERR_INVALID_ARG, "min_blocks must be >= 0");
   const long long rows = (long long)n_heads * n_q_blocks;
   if (rows > 0x7fffffffLL) return fail(BSA_ERR_INVALID_ARG, "problem too large");
-  hipLaunchKernelGGL(topp_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, scores, n_k_blocks,
-                     n_words(n_k_blocks), p, min_blocks, mask_bits);
+  const dim3 grid((unsigned)rows), block(NT);
+  const int W = n_words(n_k_blocks);
+  if (n_k_blocks <= NT)
+    hipLaunchKernelGGL(topp_kernel<1>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 2 * NT)
+    hipLaunchKernelGGL(topp_kernel<2>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 4 * NT)
+    hipLaunchKernelGGL(topp_kernel<4>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 8 * NT)
+    hipLaunchKernelGGL(topp_kernel<8>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
+  else
+    hipLaunchKernelGGL(topp_kernel<16>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
   BSA_CHECK_HIP(hipGetLastError());
   return ok();
 }
