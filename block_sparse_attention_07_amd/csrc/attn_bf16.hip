@@ -113,8 +113,12 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const u16* __restrict_
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
+// QB = query blocks per workgroup.  QB = 1: one row (64 queries) per
+// workgroup of 4 waves, two workgroups per CU.  QB = 2: two query blocks whose
+// mask rows are identical share every K/V tile; 8 waves, one workgroup per CU
+// (the same waves per SIMD), and each tile is fetched once for 128 queries.
+template <int D, int QB>
+__global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int wg_offset,
     int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
@@ -139,15 +143,32 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int qb = wave >> 2;         // query block of the pair (0 when QB = 1)
   const int rh = wave & 1;
-  const int kh = wave >> 1;
+  const int kh = (wave >> 1) & 1;
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  int row_id = wg_offset + blockIdx.x;
-  if (order) {
-    row_id = order[row_id];
-    if (row_id < 0 || row_id >= n_heads * nb) return;
+  // Work entries: e in [0, H nb) is the single row e; e in [H nb, 2 H nb) is the
+  // pair of rows e - H nb and e - H nb + 1 (identical mask rows, the first even).
+  // The planner writes each head's entries into the head's segment of nb
+  // slots: pairs first, then singles, then -1.  QB = 1 workgroups run the
+  // singles; QB = 2 workgroup b reads slot b % (nb/2) of segment b / (nb/2).
+  const int total_rows = n_heads * nb;
+  int row_id;
+  if constexpr (QB == 1) {
+    row_id = wg_offset + blockIdx.x;
+    if (order) {
+      row_id = order[row_id];
+      if (row_id < 0 || row_id >= total_rows) return;
+    }
+  } else {
+    const int half = nb >> 1;
+    const int b = wg_offset + blockIdx.x;
+    const int e = order[(b / half) * nb + (b % half)];
+    if (e < total_rows || e >= 2 * total_rows) return;
+    row_id = e - total_rows;
+    if ((row_id % nb) & 1 || (row_id % nb) + 1 >= nb) return;
   }
   const int h = row_id / nb;
   const int u = row_id - h * nb;
@@ -163,7 +184,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   {
     // Rows past the sequence end read the last real row (always in bounds) and
     // are zeroed by a select on the loaded value.
-    const int qrow = BLK * u + 32 * rh + r32;
+    const int qrow = BLK * (u + qb) + 32 * rh + r32;
     const bool qvalid = qrow < N;
     const int qsrc = qvalid ? qrow : N - 1;
 #pragma unroll
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   // the chunk the swizzle stores there.  Each wave issues NI instructions per
   // tensor and tile.
   constexpr int KR = 1024 / (2 * D);                  // K rows per DMA instruction
-  constexpr int NI = D / 32;                          // DMA instructions per wave and tensor
+  constexpr int NI = D / (32 * QB);                    // DMA instructions per wave and tensor
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   int k_voff[NI], v_voff[NI];
 #pragma unroll
@@ -390,14 +411,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     // stages.  Past the end of the list the last tile is used again (loads stay
     // unconditional; the extra S is discarded).
     auto tile = [&](int t) { return __builtin_amdgcn_readfirstlane(list[min(t, n - 1)]); };
+    // only the last block of the sequence can be ragged, and it is always the
+    // last entry of an ascending list
     kdma(tile(0), 0);
     vdma(tile(0), 0);
     __syncthreads();
     kdma(tile(1), 1);
     f32x16 s_cur = qk(0);
     __syncthreads();
-    // only the last block of the sequence can be ragged, and it is always the
-    // last entry of an ascending list
     // The loop is unrolled by two so each step's stage indices are constants and
     // every LDS address is a per-lane base plus an instruction offset.
     auto body = [&](int t, auto parity) {
@@ -414,28 +435,34 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   }
 
   // Merge the two key halves of each query-row half and write the output.
-  // mo(rh)[accumulator register][lane] overlays V^T stage rh (both 128 * D
-  // bytes); mm / ml overlay the block list.
+  // mo(j)[accumulator register][lane], j = 2 qb + rh, overlays one tile stage
+  // (each 128 * D bytes): the V^T stages for one query block, also the K
+  // stages for a pair; mm / ml overlay the block list.
   static_assert(sizeof(vts0) == (D / 2) * 64 * sizeof(float), "merge overlay size");
-  auto mo = [&](int half) { return reinterpret_cast<float (*)[64]>(half ? vts1 : vts0); };
+  static_assert(sizeof(list) >= 2 * 2 * QB * 32 * sizeof(float), "merge overlay size");
+  auto mo = [&](int j) {
+    u16* b = j == 0 ? vts0 : (j == 1 ? vts1 : (j == 2 ? kst0 : kst1));
+    return reinterpret_cast<float (*)[64]>(b);
+  };
+  const int mj = 2 * qb + rh;
   auto mm = reinterpret_cast<float (*)[32]>(list);
-  auto ml = reinterpret_cast<float (*)[32]>(list) + 2;
+  auto ml = reinterpret_cast<float (*)[32]>(list) + 2 * QB;
   __syncthreads();
   const float l_row = l_part + __shfl_xor(l_part, 32);
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mo(rh)[16 * db + i][lane] = o[db][i];
+      for (int i = 0; i < 16; ++i) mo(mj)[16 * db + i][lane] = o[db][i];
     if (g == 0) {
-      mm[rh][r32] = m_run;
-      ml[rh][r32] = l_row;
+      mm[mj][r32] = m_run;
+      ml[mj][r32] = l_row;
     }
   }
   __syncthreads();
   if (kh == 0) {
-    const float m1 = mm[rh][r32];
-    const float l1 = ml[rh][r32];
+    const float m1 = mm[mj][r32];
+    const float l1 = ml[mj][r32];
     const float mm = fmaxf(m_run, m1);
     float a0 = 0.f, a1 = 0.f;
     if (mm != -INFINITY) {
@@ -444,7 +471,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     }
     const float L = l_row * a0 + l1 * a1;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    const int row = BLK * u + 32 * rh + r32;
+    const int row = BLK * (u + qb) + 32 * rh + r32;
     if (row < N) {
       u16* orow = O + head_off + (size_t)row * D;
 #pragma unroll
@@ -455,7 +482,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * q4 + r;
-            y[r] = (__bf16)((o[db][i] * a0 + mo(rh)[16 * db + i][lane] * a1) * inv);
+            y[r] = (__bf16)((o[db][i] * a0 + mo(mj)[16 * db + i][lane] * a1) * inv);
           }
           *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * q4 + 4 * g) = y;
         }
@@ -474,7 +501,7 @@ int generation_size() {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<D>, NT, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<D, 1>, NT, 0) != hipSuccess ||
       cus <= 0 || per_cu <= 0)
     return 0;
   cache[dev] = cus * per_cu;
@@ -495,12 +522,19 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   // lets start times drift apart after the first wave of workgroups retires,
   // and the tiles in use then spread over the whole head.  Without an order
   // the grid goes out in one launch.
+  // Pair entries (two query blocks with identical mask rows) go first, in one
+  // launch of 128-query workgroups over the pair slots of every head segment.
   const int total = n_heads * nb;
+  if (order && nb >= 2) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3((unsigned)(n_heads * (nb / 2))), dim3(2 * NT), 0,
+                       stream, Q, K, VT, mask, order, 0, n_heads, seq_len, nb, W, c, O);
+    BSA_CHECK_HIP(hipGetLastError());
+  }
   int gen = order ? generation_size<D>() : 0;
   if (gen <= 0) gen = total;
   for (int off = 0; off < total; off += gen) {
     const int count = min(gen, total - off);
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
                        mask, order, off, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());
   }

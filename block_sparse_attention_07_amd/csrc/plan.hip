@@ -2,7 +2,8 @@
 //
 // The packed row mask (ScalingAttention, section 4.3.2) already tells how many
 // kept tiles each (head, query block) row will run; a popcount pass turns that
-// into a schedule.  Heads run in decreasing total work so the heaviest heads are
+// into a schedule, and adjacent rows with identical masks are paired so that
+// one workgroup serves both.  Heads run in decreasing total work so the heaviest heads are
 // dispatched first and the lightest fill the tail.  Within a head, rows run in
 // decreasing kept-block count: the workgroups resident at the same time then
 // hold rows of nearly equal length, start together, walk their ascending tile
@@ -32,16 +33,22 @@ __global__ void row_counts_kernel(const uint64_t* __restrict__ mask, int n_rows,
 }
 
 // One workgroup per head: rank the head among all heads (more work first, ties
-// by head index), then rank each of its rows within the head (more kept blocks
-// first, ties by query block) and write row ids at those positions.
-constexpr int SORT_MAX_NB = 8192;   // rows per head ranked in LDS; longer heads keep u order
+// by head index), then lay out the head's segment of nb work slots.  Adjacent
+// query blocks (u, u+1), u even, whose mask rows are identical become one pair
+// entry (2 H nb ... : value H nb + h nb + u), processed by 128-query workgroups;
+// the other rows are single entries (h nb + u); the slots freed by pairs hold -1.
+// Within the segment: pairs, then singles, each in decreasing kept-block count
+// (ties by query block), then the -1 slots.
+constexpr int SORT_MAX_NB = 8192;   // rows per head ranked in LDS; longer heads keep u order, no pairs
 
 __global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restrict__ head_tiles,
                                                          const int32_t* __restrict__ counts,
-                                                         int n_heads, int nb,
+                                                         const uint64_t* __restrict__ mask,
+                                                         int n_heads, int nb, int W, uint64_t lastmask,
                                                          int32_t* __restrict__ order) {
   __shared__ int partial[256];
-  __shared__ int cnt[SORT_MAX_NB];
+  __shared__ int key[SORT_MAX_NB];
+  __shared__ unsigned char pair[SORT_MAX_NB / 2];
   const int h = blockIdx.x;
   const int64_t mine = head_tiles[h];
   int before = 0;
@@ -51,8 +58,18 @@ __global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restri
   }
   partial[threadIdx.x] = before;
   const bool sort_rows = nb <= SORT_MAX_NB;
-  if (sort_rows)
-    for (int u = threadIdx.x; u < nb; u += blockDim.x) cnt[u] = counts[(size_t)h * nb + u];
+  if (sort_rows) {
+    for (int i = threadIdx.x; i < nb / 2; i += blockDim.x) {
+      const uint64_t* r0 = mask + ((size_t)h * nb + 2 * i) * W;
+      const uint64_t* r1 = r0 + W;
+      bool eq = true;
+      for (int w = 0; w < W && eq; ++w) {
+        const uint64_t m = (w == W - 1) ? lastmask : ~0ull;
+        eq = ((r0[w] ^ r1[w]) & m) == 0;
+      }
+      pair[i] = eq;
+    }
+  }
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) partial[threadIdx.x] += partial[threadIdx.x + s];
@@ -60,17 +77,27 @@ __global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restri
   }
   const int rank = partial[0];
   int32_t* dst = order + (size_t)rank * nb;
+  const int total = n_heads * nb;
+  if (!sort_rows) {
+    for (int u = threadIdx.x; u < nb; u += blockDim.x) dst[u] = h * nb + u;
+    return;
+  }
+  // sort key: class (0 pair lead, 1 single, 2 pair follower), then count descending
   for (int u = threadIdx.x; u < nb; u += blockDim.x) {
-    int r = u;
-    if (sort_rows) {
-      const int cu = cnt[u];
-      r = 0;
-      for (int j = 0; j < nb; ++j) {
-        const int cj = cnt[j];
-        r += (cj > cu) || (cj == cu && j < u);
-      }
+    const bool paired = (u >> 1) < nb / 2 && pair[u >> 1];
+    const int cls = paired ? ((u & 1) ? 2 : 0) : 1;
+    key[u] = (cls << 15) + (16383 - counts[(size_t)h * nb + u]);
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < nb; u += blockDim.x) {
+    const int ku = key[u];
+    int r = 0;
+    for (int j = 0; j < nb; ++j) {
+      const int kj = key[j];
+      r += (kj < ku) || (kj == ku && j < u);
     }
-    dst[r] = h * nb + u;
+    const int cls = ku >> 15;
+    dst[r] = cls == 0 ? total + h * nb + u : (cls == 1 ? h * nb + u : -1);
   }
 }
 
@@ -89,8 +116,8 @@ int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts,
   hipLaunchKernelGGL(row_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, mask, rows,
                      nb, W, lastmask, counts, head_tiles);
   BSA_CHECK_HIP(hipGetLastError());
-  hipLaunchKernelGGL(head_order_kernel, dim3(n_heads), dim3(256), 0, stream, head_tiles, counts,
-                     n_heads, nb, order);
+  hipLaunchKernelGGL(head_order_kernel, dim3(n_heads), dim3(256), 0, stream, head_tiles, counts, mask,
+                     n_heads, nb, W, lastmask, order);
   BSA_CHECK_HIP(hipGetLastError());
   return ok();
 }

@@ -99,11 +99,16 @@ int sparse_attn_fwd_f32(const float* q, const float* k, const float* v, const ui
  *   mask_bits   uint64 [n_heads][nb][W], read only.
  *   row_counts  int32 [n_heads * nb], written: kept blocks of each (head, query block) row.
  *   head_tiles  int64 [n_heads], written: kept blocks of each head.
- *   work_order  int32 [n_heads * nb], written: a permutation of row ids (h * nb + u):
- *               heads in decreasing head_tiles (ties by head index); within a head,
- *               rows in decreasing row_counts (ties by increasing u) when nb <= 8192,
- *               else in increasing u.  Rows of equal length then run side by side,
- *               which keeps their tile walks in step and their K/V in the L2 cache.
+ *   work_order  int32 [n_heads * nb], written: work entries, one segment of nb
+ *               slots per head, heads in decreasing head_tiles (ties by head index).
+ *               Entry values: h * nb + u is the single row u of head h;
+ *               n_heads * nb + h * nb + u (u even) is the pair of rows u, u + 1, whose
+ *               mask rows are identical, run by one 128-query workgroup that fetches
+ *               each K/V tile once for both; -1 is an empty slot.  Within a segment:
+ *               pairs, then singles, each in decreasing row_counts (ties by increasing
+ *               u), then the -1 slots.  When nb > 8192 the segment lists the single
+ *               rows in increasing u (no pairs).  Rows of equal length then run side by
+ *               side, which keeps their tile walks in step and their K/V in L2.
  */
 int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int block,
                      int32_t* row_counts, int64_t* head_tiles, int32_t* work_order,
@@ -111,12 +116,16 @@ int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int bl
 
 /*
  * sparse_attn_fwd_planned -- sparse_attn_fwd with a caller-provided work order
- * (any permutation of [0, n_heads * nb), normally from sparse_attn_plan).  Entries
- * outside [0, n_heads * nb) are skipped.  The transposed copy of V uses the
+ * (normally from sparse_attn_plan).  Single entries h * nb + u may appear anywhere;
+ * pair entries (see sparse_attn_plan) are read only from the first nb / 2 slots of
+ * each nb-slot segment, and the two rows of a pair must have identical mask rows.
+ * Every row must be covered exactly once; other values are skipped.  A plain
+ * permutation of [0, n_heads * nb) is a valid order.  The transposed copy of V uses the
  * library's per-device scratch buffer (see sparse_attn_fwd about overlapping calls).
- * After the transpose, the rows are enqueued as consecutive kernel launches of one
- * device-full of workgroups each (compute units x resident workgroups per unit), in
- * the order given, so that the rows of each slice start together.
+ * After the transpose, the pair entries run in one launch, then the single entries as
+ * consecutive kernel launches of one device-full of workgroups each (compute units x
+ * resident workgroups per unit), in the order given, so that the rows of each slice
+ * start together.
  */
 int sparse_attn_fwd_planned(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
                             const int32_t* work_order, int n_heads, int seq_len, int head_dim,

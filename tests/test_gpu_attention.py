@@ -153,8 +153,8 @@ def test_empty_rows_padding_bits_plan_and_determinism():
                           work_order=order)
     torch.cuda.synchronize()
     assert np.array_equal(gu.bf16_host(out), a)
-    # any permutation of the rows gives the same bits
-    rev = torch.flip(order, [0]).contiguous()
+    # any permutation of the rows gives the same bits (single entries only)
+    rev = torch.arange(3 * nb - 1, -1, -1, dtype=torch.int32, device=order.device)
     out2 = bsa.sparse_attn(gu.to_dev(q, True), gu.to_dev(k, True), gu.to_dev(v, True), mdev, scale,
                            work_order=rev)
     torch.cuda.synchronize()
@@ -174,8 +174,18 @@ def test_plan_order_is_heads_by_decreasing_work():
     t = keep.reshape(H, -1).sum(1)
     rc = keep.sum(2)
     heads = sorted(range(H), key=lambda h: (-t[h], h))
-    want = np.concatenate([h * nb + np.array(sorted(range(nb), key=lambda u: (-rc[h, u], u))) for h in heads])
-    assert np.array_equal(order.cpu().numpy(), want)
+    # each head's segment: pairs of identical adjacent rows (u even) first, then the
+    # other rows, each by decreasing count (ties by u), then -1 for the slots pairs free
+    want = []
+    for h in heads:
+        paired = [u for u in range(0, nb - 1, 2) if np.array_equal(keep[h, u], keep[h, u + 1])]
+        covered = set(paired) | {u + 1 for u in paired}
+        singles = [u for u in range(nb) if u not in covered]
+        want += [H * nb + h * nb + u for u in sorted(paired, key=lambda u: (-rc[h, u], u))]
+        want += [h * nb + u for u in sorted(singles, key=lambda u: (-rc[h, u], u))]
+        want += [-1] * len(paired)
+    assert sum(np.array_equal(keep[3, u], keep[3, u + 1]) for u in range(0, nb - 1, 2)) == nb // 2
+    assert np.array_equal(order.cpu().numpy(), np.array(want))
     assert np.array_equal(tiles.cpu().numpy(), t)
     assert np.array_equal(counts.cpu().numpy(), rc.reshape(-1))
 
@@ -237,3 +247,37 @@ def test_hunyuan_stripe_pipeline():
     out = got.cpu()
     for (h, u), r in zip(blocks, ref):
         gu.assert_bf16_close(gu.bf16_host(out[h, u * B:u * B + r.shape[0]]), r, f"hunyuan ({h},{u})")
+
+
+@pytest.mark.parametrize("n,d", [(64 * 37 + 13, 128), (64 * 40, 64), (64 * 9 + 1, 128)])
+def test_pairs_of_identical_rows(n, d):
+    """Adjacent query blocks with identical mask rows run as one 128-query workgroup
+    (planner pair entries); some pairs, some singles, empty pairs, a ragged last
+    block inside a pair, all rows compared with the oracle."""
+    nb = -(-n // B)
+    H = 3
+    q, k, v = _rand_bf16(H, n, d, seed=n + d)
+    rng = np.random.default_rng(n)
+    keep = rng.random((H, nb, nb)) < 0.3
+    for h in range(H):
+        for u in range(0, nb - 1, 2):
+            if rng.random() < 0.6:
+                keep[h, u + 1] = keep[h, u]
+    keep[1, :] = True                      # a full head: every row paired
+    keep[2, 0:2] = False                   # an empty pair
+    if nb % 2 == 0:
+        keep[0, nb - 1] = keep[0, nb - 2]  # the ragged last block inside a pair
+    bits = crm.pack_rows(keep)
+    _, _, order = bsa.plan(gu.to_dev(bits), n)
+    o = order.cpu().numpy()
+    assert (o >= H * nb).sum() > 0 and (o == -1).sum() == (o >= H * nb).sum()
+    got = _run_bf16(q, k, v, bits, 1 / np.sqrt(d))
+    ref = sparse_attention(_f(q), _f(k), _f(v), bits, 1 / np.sqrt(d))
+    for h in range(H):
+        gu.assert_bf16_close(got[h], ref[h], f"head {h}")
+    assert np.all(got[2, :128] == 0)
+    # the same result through a plain permutation (no pair entries)
+    perm = gu.to_dev(np.random.default_rng(1).permutation(H * nb).astype(np.int32))
+    got2 = _run_bf16(q, k, v, bits, 1 / np.sqrt(d), work_order=perm)
+    for h in range(H):
+        gu.assert_bf16_close(got2[h], ref[h], f"head {h} permuted")
