@@ -7,10 +7,10 @@ set bits of a row in ascending order: it skips all-zero words (advancing a base
 index by the word width per word), reports base + count-trailing-zeros of the
 current word, and clears the lowest set bit to advance.
 
-The pages use 32-bit words with 128-token blocks; this library stores 64-bit
-words with 64-token blocks.  Word ``w`` bit ``b`` (least significant bit = 0)
-is key block ``64 w + b``; bits at positions >= n_blocks are padding and carry
-no meaning.
+The pages use 32-bit words with 128-token blocks; the library's main format is
+64-bit words with 64-token blocks, and it also takes the pages' format.  Word
+``w`` bit ``b`` (least significant bit = 0) is key block ``word_bits * w + b``;
+bits at positions >= n_blocks are padding and carry no meaning.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 """
@@ -59,6 +59,26 @@ def unpack_rows(mask_bits: np.ndarray, n_blocks: int) -> np.ndarray:
     bits = (m[..., :, None] >> shifts) & np.uint64(1)           # [..., n_q, W, 64]
     bits = bits.reshape(m.shape[:-1] + (m.shape[-1] * 64,))
     return bits[..., :n_blocks].astype(bool)
+
+
+def unpack_rows32(mask_words: np.ndarray, n_blocks: int) -> np.ndarray:
+    """Decode the pages' 32-bit words [..., n_q, W] into a boolean mask
+    [..., n_q, n_blocks] (bit b of word w is key block 32 w + b)."""
+    m = np.ascontiguousarray(mask_words, dtype=np.uint32)
+    shifts = np.arange(32, dtype=np.uint32)
+    bits = (m[..., :, None] >> shifts) & np.uint32(1)           # [..., n_q, W, 32]
+    bits = bits.reshape(m.shape[:-1] + (m.shape[-1] * 32,))
+    return bits[..., :n_blocks].astype(bool)
+
+
+def refine_blocks(keep: np.ndarray, factor: int, n_fine: int) -> np.ndarray:
+    """The same block mask over blocks ``factor`` times smaller: fine block pair
+    (u, v) is kept exactly when coarse pair (u // factor, v // factor) is.
+    ``n_fine`` = ceil(N / fine block) may be less than factor * n_coarse when the
+    last coarse block is short."""
+    keep = np.asarray(keep, dtype=bool)
+    u = np.arange(n_fine) // factor
+    return keep[..., u[:, None], u[None, :]]
 
 
 def pack_rows(keep: np.ndarray) -> np.ndarray:

@@ -104,6 +104,19 @@ def pack_bits(keep: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(by).view("<u8").reshape(keep.shape[:-1] + (wd,))
 
 
+def pack_bits32(keep: np.ndarray) -> np.ndarray:
+    """Pack a boolean block mask [..., nq, nk] into uint32 words [..., nq, ceil(nk/32)]
+    (the 32-bit row-mask format), block b at bit (b % 32) of word (b // 32)."""
+    keep = np.asarray(keep, dtype=bool)
+    nk = keep.shape[-1]
+    wd = -(-nk // 32)
+    pad = wd * 32 - nk
+    if pad:
+        keep = np.concatenate([keep, np.zeros(keep.shape[:-1] + (pad,), bool)], axis=-1)
+    by = np.packbits(keep, axis=-1, bitorder="little")
+    return np.ascontiguousarray(by).view("<u4").reshape(keep.shape[:-1] + (wd,))
+
+
 def _fill_random(rng, keep_row_major: np.ndarray, target: int) -> None:
     """Set uniformly random extra cells (without replacement) among the cells that
     are still off, until ``target`` cells are on (no-op when already there)."""
