@@ -1,7 +1,7 @@
 """Benchmark: block-sparse attention at the Wan2.1-14B 720p layer shape on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
-                    [--sweep] [--aux]
+                    [--sweep] [--aux] [--b128]
 
 Workload (synthetic, seeded): 40 heads, head_dim 128, bf16, latent grid
 21x45x80 = 75,600 tokens (1182 blocks of 64); 8 heads keep every block, the
@@ -23,6 +23,8 @@ Reported on one JSON line:
          shape: speedup against 1/density (the analogue of ScalingAttention Fig. 5).
 --aux    (extra, to stderr) the HBM-bound kernels of the path (mask producers,
          block scores, top-p, permutation, resize, fidelity) in GB/s vs 8 TB/s.
+--b128   (extra, to stderr) the same layer under the same mask recipe drawn over
+         128x128-token blocks and passed as 32-bit row words (the pages' format).
 """
 from __future__ import annotations
 
@@ -131,6 +133,25 @@ def density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
         del md
 
 
+def b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
+    """The same layer with the mask recipe drawn over the pages' 128-token blocks,
+    passed as 32-bit row words.  Flops count the kept 64-token tiles of the same
+    mask (the expanded form), as the headline metric does."""
+    import workloads
+    keep = workloads.mask_wan14b(w, block=128)
+    words = workloads.pack_bits32(keep)
+    wd = torch.from_numpy(words.view(np.int32)).to(qd.device)
+    m64 = bsa.mask_b128_to_b64(wd, w.seq_len)
+    kept = int(sum(int(x).bit_count() for x in m64.cpu().numpy().view(np.uint64).ravel()))
+    f = lambda: bsa.sparse_attn_b128(qd, kd, vd, wd, w.scale, out=out)
+    f()
+    ms = timed(f, 10)
+    print(json.dumps({"b128_layer": "Wan2.1-14B 720p, 128x128 blocks, 32-bit words",
+                      "density": round(float(keep.mean()), 4), "kept_64_tiles": kept, "ms": round(ms, 3),
+                      "tflops": round(kept * tile_flops(w.head_dim) / (ms * 1e-3) / 1e12, 1),
+                      "speedup_vs_full": round(ms_full / ms, 3)}), file=sys.stderr, flush=True)
+
+
 def aux_kernels(bsa, torch, timed):
     """Effective bandwidth of the HBM-bound kernels on the configs' shapes."""
     dev = torch.device("cuda", 0)
@@ -186,6 +207,8 @@ def main():
                     help="short run for counter collection: a few planned launches plus a 1 GiB copy")
     ap.add_argument("--sweep", action="store_true", help="also run the density sweep (stderr)")
     ap.add_argument("--aux", action="store_true", help="also time the HBM-bound kernels (stderr)")
+    ap.add_argument("--b128", action="store_true",
+                    help="also time the layer under a 128x128-block mask in 32-bit words (stderr)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -291,6 +314,8 @@ def main():
         density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
     if args.aux:
         aux_kernels(bsa, torch, timed)
+    if args.b128:
+        b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, bits, keep)
     else:

@@ -4,7 +4,8 @@
 
 computes softmax(scale * Q K^T + M) V where M is 0 on the 64x64 blocks whose bit
 is set in the per-head packed row mask and -inf elsewhere (ScalingAttention,
-section 4.3.2).  Mask producers: ``mask_from_stripes`` (PSA stripe tuples),
+section 4.3.2); ``sparse_attn_b128`` takes the pages' own format, 128x128 blocks
+in 32-bit words.  Mask producers: ``mask_from_stripes`` (PSA stripe tuples),
 ``block_scores_meanpool`` + ``mask_from_block_scores_topp`` (online top-p with a
 top-k minimum), ``mask_from_threshold_map`` (static masks M = I(T <= p*)) with
 ``threshold_map_resize`` / ``mask_resize`` for other resolutions, and
@@ -18,6 +19,7 @@ from .api import (  # noqa: F401
     attn_fidelity,
     block_scores_meanpool,
     hilbert3d_order,
+    mask_b128_to_b64,
     mask_from_block_scores_topp,
     mask_from_stripes,
     mask_from_threshold_map,
@@ -26,6 +28,7 @@ from .api import (  # noqa: F401
     permute_tokens,
     plan,
     sparse_attn,
+    sparse_attn_b128,
     threshold_map_resize,
 )
 from ._lib import BsaError, LIB_PATH  # noqa: F401

@@ -22,6 +22,8 @@ SIGNATURES = {
     "sparse_attn_fwd_f32": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],
     "sparse_attn_plan": [_p, _i, _i, _i, _p, _p, _p, _p],
     "sparse_attn_fwd_planned": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],
+    "sparse_attn_fwd_b128": [_p, _p, _p, _p, _i, _i, _i, _f, _p, _p],
+    "mask_b128_to_b64": [_p, _i, _i, _p, _p],
     "mask_from_stripes": [_p, _i, _i, _i, _i, _i, _p, _p],
     "block_scores_meanpool": [_p, _p, _i, _i, _i, _i, _f, _p, _p],
     "mask_from_block_scores_topp": [_p, _i, _i, _i, _f, _i, _p, _p],

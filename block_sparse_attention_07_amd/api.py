@@ -5,7 +5,9 @@ contiguity, allocates outputs with torch (device memory is the only thing torch
 provides here) and passes raw pointers plus torch's current HIP stream to the
 library.  All computation happens in the library's kernels.
 
-Masks travel as torch.int64 tensors holding the uint64 words bit for bit.
+Masks travel as torch.int64 tensors holding the uint64 words bit for bit (and,
+for the 32-bit format over 128-token blocks, torch.int32 tensors holding the
+uint32 words).
 """
 from __future__ import annotations
 
@@ -87,6 +89,50 @@ def sparse_attn(q, k, v, mask_bits, scale=None, out=None, work_order=None):
         check(rc, "sparse_attn_fwd_f32")
     else:
         raise ValueError("q, k, v must be bfloat16 or float32")
+    return out
+
+
+def _check_mask32(mask_words, H, N):
+    nb = -(-N // 128)
+    W = -(-nb // 32)
+    _need(mask_words.dtype == torch.int32, "mask_words must be int32 (uint32 words)")
+    _need(tuple(mask_words.shape) == (H, nb, W),
+          f"mask_words must be [{H}, {nb}, {W}], got {tuple(mask_words.shape)}")
+
+
+def sparse_attn_b128(q, k, v, mask_words, scale=None, out=None):
+    """Block-sparse attention over 128 x 128-token blocks with 32-bit row-mask words
+    (sparse_attn_fwd_b128).  q, k, v: bf16 [H, N, d]; mask_words int32
+    [H, ceil(N/128), ceil(ceil(N/128)/32)]."""
+    _dev(q, k, v, mask_words)
+    _need(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must share shape [H, N, d]")
+    _need(q.dtype == k.dtype == v.dtype == torch.bfloat16, "q, k, v must be bfloat16")
+    H, N, d = q.shape
+    _check_mask32(mask_words, H, N)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(q, out)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    rc = lib().sparse_attn_fwd_b128(_ptr(q), _ptr(k), _ptr(v), _ptr(mask_words), H, N, d, scale,
+                                    _ptr(out), _stream(q))
+    check(rc, "sparse_attn_fwd_b128")
+    return out
+
+
+def mask_b128_to_b64(mask_words, seq_len: int, out=None):
+    """32-bit rows over 128-token blocks -> the same mask as 64-bit rows over
+    64-token blocks (int64 [H, ceil(N/64), ceil(ceil(N/64)/64)])."""
+    _dev(mask_words)
+    H = mask_words.shape[0]
+    _check_mask32(mask_words, H, seq_len)
+    nb = -(-seq_len // BLOCK)
+    if out is None:
+        out = torch.empty((H, nb, mask_words.shape[2]), dtype=torch.int64, device=mask_words.device)
+    _dev(mask_words, out)
+    _check_mask(out, H, seq_len)
+    rc = lib().mask_b128_to_b64(_ptr(mask_words), H, int(seq_len), _ptr(out), _stream(mask_words))
+    check(rc, "mask_b128_to_b64")
     return out
 
 

@@ -35,6 +35,7 @@ SOURCES = [
     "threshold.hip",
     "fidelity.hip",
     "resize.hip",
+    "b128.hip",
 ]
 EXTRA_FLAGS = {"topp.hip": ["-ffp-contract=off"]}
 

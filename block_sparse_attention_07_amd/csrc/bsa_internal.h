@@ -29,7 +29,11 @@ inline int n_words(int nb) { return (nb + 63) / 64; }
 // Checks shared by the attention entry points.
 int check_attn_args(const void* q, const void* k, const void* v, const void* mask, const void* out,
                     int n_heads, int seq_len, int head_dim, int block_q, int block_k, float scale,
-                    size_t elem_align);
+                    size_t elem_align, size_t mask_align = 8);
+// Expand 32-bit rows over 128-token blocks into 64-bit rows over 64-token blocks
+// (b128.hip).
+int launch_expand_b128(const uint32_t* mask_words, int n_heads, int seq_len, uint64_t* mask_bits,
+                       hipStream_t stream);
 
 // Launch the row-count / head-order planner (defined in plan.hip).
 int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts, int64_t* head_tiles,

@@ -80,12 +80,13 @@ void* scratch(size_t bytes, hipStream_t stream) {
 
 int check_attn_args(const void* q, const void* k, const void* v, const void* mask, const void* out,
                     int n_heads, int seq_len, int head_dim, int block_q, int block_k, float scale,
-                    size_t elem_align) {
+                    size_t elem_align, size_t mask_align) {
   if (!q || !k || !v || !mask || !out) return fail(BSA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(q, elem_align) || !aligned(k, elem_align) || !aligned(v, elem_align) ||
       !aligned(out, elem_align))
     return fail(BSA_ERR_INVALID_ARG, "q, k, v and out must be %zu-byte aligned", elem_align);
-  if (!aligned(mask, 8)) return fail(BSA_ERR_INVALID_ARG, "mask_bits must be 8-byte aligned");
+  if (!aligned(mask, mask_align))
+    return fail(BSA_ERR_INVALID_ARG, "the mask must be %zu-byte aligned", mask_align);
   if (n_heads < 1 || seq_len < 1)
     return fail(BSA_ERR_INVALID_ARG, "n_heads (%d) and seq_len (%d) must be >= 1", n_heads, seq_len);
   if (block_q != 64 || block_k != 64)

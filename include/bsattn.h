@@ -132,6 +132,38 @@ int sparse_attn_fwd_planned(const void* q, const void* k, const void* v, const u
                             int block_q, int block_k, float scale, void* out, hipStream_t stream);
 
 /*
+ * sparse_attn_fwd_b128 -- sparse_attn_fwd with the pages' own mask format:
+ * 128 x 128-token blocks, each row packed in 32-bit words (ScalingAttention section
+ * 4.3.2: one uint32 load decodes 32 KV blocks; Appendix E, Algorithm 2 steps its
+ * base by 32 per word).
+ *
+ *   q, k, v, out  as sparse_attn_fwd (bf16 [n_heads][seq_len][head_dim]).
+ *   mask_words    uint32 [n_heads][nb128][W], nb128 = ceil(seq_len / 128),
+ *                 W = ceil(nb128 / 32) (= bsa_mask_words(seq_len, 64)); bit b of
+ *                 word w is key block 32 w + b; padding bits are ignored.  4-byte
+ *                 aligned, read only.
+ * Keys and queries of the last, possibly short, 128-block are its real tokens only.
+ * The mask is expanded (mask_b128_to_b64) into the library's per-device scratch
+ * buffer; the two 64-token halves of every 128-row then form a pair in the work
+ * order, so each K/V tile is fetched once per 128 queries.  Scratch and error
+ * behaviour as sparse_attn_fwd.  Rows pair only while ceil(seq_len / 64) <= 8192.
+ */
+int sparse_attn_fwd_b128(const void* q, const void* k, const void* v, const uint32_t* mask_words,
+                         int n_heads, int seq_len, int head_dim, float scale, void* out,
+                         hipStream_t stream);
+
+/*
+ * mask_b128_to_b64 -- the same mask rewritten over 64-token blocks: 64-block (u, v)
+ * is kept iff 128-block (u / 2, v / 2) is.  Word w of a 32-bit row and word w of a
+ * 64-bit row cover the same tokens, so the expansion is word for word.
+ *   mask_words  uint32 [n_heads][ceil(seq_len/128)][W], read only (W as above).
+ *   mask_bits   uint64 [n_heads][ceil(seq_len/64)][W], written in full (padding
+ *               bits zero).
+ */
+int mask_b128_to_b64(const uint32_t* mask_words, int n_heads, int seq_len, uint64_t* mask_bits,
+                     hipStream_t stream);
+
+/*
  * mask_from_stripes -- expand per-head PSA stripe tuples into packed row masks.
  * PSA page, Figure 3 and Appendix Tables 7-9: per head either "full window" or a
  * temporal (width, offset, stride) and a spatial (width, offset, stride) stripe.

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     assert sorted(names) == sorted(_lib.EXPORTS)
 
 
@@ -99,3 +99,29 @@ def test_hilbert_order_matches_oracle():
         perm = np.empty(T * H * W, np.int32)
         assert L.hilbert3d_order(T, H, W, perm.ctypes.data_as(ctypes.c_void_p)) == 0
         assert np.array_equal(perm, hilbert.hilbert_order(T, H, W))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(m=0), 1), (dict(N=0), 1), (dict(H=0), 1), (dict(d=96), 2),
+    (dict(scale=float("inf")), 1), (dict(scale=0.0), 1),
+])
+def test_b128_attention_argument_errors_precede_any_device_call(kw, code):
+    a = _attn_args(**kw)
+    args = a[:7] + a[9:]          # no block_q / block_k: the format fixes them
+    L = _lib.lib()
+    assert L.sparse_attn_fwd_b128(*args) == code
+    assert L.bsa_last_error().decode()
+
+
+def test_b128_mask_alignment_and_expansion_argument_errors():
+    L = _lib.lib()
+    a = _attn_args()
+    args = list(a[:7] + a[9:])
+    args[3] = ctypes.c_void_p(16 * 8 + 2)       # 32-bit words need 4-byte alignment
+    assert L.sparse_attn_fwd_b128(*args) == 1
+    assert "aligned" in L.bsa_last_error().decode()
+    p = ctypes.c_void_p
+    assert L.mask_b128_to_b64(None, 1, 128, p(256), None) == 1
+    assert L.mask_b128_to_b64(p(256), 1, 128, p(260), None) == 1      # uint64 output misaligned
+    assert L.mask_b128_to_b64(p(256), 0, 128, p(256), None) == 1
+    assert L.mask_b128_to_b64(p(256), 1, 0, p(256), None) == 1
