@@ -272,11 +272,12 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
     if (may_be_ragged) {
       const int hi = N - vb * BLK;   // tile positions >= hi lie past the sequence end
       if (hi < BLK) {
+        // key of register i = lane base + a constant; compare the base with a
+        // scalar threshold per register
+        const int kbase = 32 * kh + 8 * g;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * kh + 16 * (i >> 3) + 8 * g + (i & 7);
-          if (key >= hi) s[i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kbase >= hi - (16 * (i >> 3) + (i & 7))) s[i] = -INFINITY;
       }
     }
     // IEEE maximum (NaN-propagating) needs no input canonicalisation and maps to
@@ -305,10 +306,26 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) sn[i] = 0.f;
     float p[16];
+    // MFMA operands in registers of their own: all K operands are read first,
+    // the V operands between the QK^T MFMAs, so no MFMA waits on a read that
+    // was issued just before it.
+    bf16x8 ka[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      ka[ks] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kstage(kbuf)) + k_rd[ks]);
+    bf16x8 va[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * db + r32;
+#pragma unroll
+      for (int s0 = 0; s0 < 2; ++s0) {
+        const int chunk = (4 * kh + 2 * s0 + g) ^ v_swz(d);
+        va[db][s0] = *reinterpret_cast<const bf16x8*>(vstage(vbuf) + d * BLK + 8 * chunk);
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kstage(kbuf)) + k_rd[ks]);
-      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sn, 0, 0, 0);
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sn, 0, 0, 0);
       if (2 * ks < 16) {
         const int i = 2 * ks;
         p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
@@ -338,21 +355,32 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
       }
       l_part += ls0 + ls1;
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the K operand read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      if (ks < 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one V operand read
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU ops
+    }
+    // Single rows: two workgroups share each SIMD, one wave of each.  Raising
+    // the wave's priority for its PV MFMAs lets them issue back to back while
+    // the other wave runs its VALU-heavy softmax, instead of interleaving both
+    // waves' MFMAs and stretching both steps.
+    if constexpr (QB == 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = 32 * db + r32;
 #pragma unroll
       for (int s0 = 0; s0 < 2; ++s0) {
-        const int chunk = (4 * kh + 2 * s0 + g) ^ v_swz(d);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vstage(vbuf) + d * BLK + 8 * chunk);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, s0 ? pb1 : pb0, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s0], s0 ? pb1 : pb0, o[db], 0, 0, 0);
       }
+    }
+    if constexpr (QB == 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     }
     return sn;
   };
@@ -410,7 +438,12 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
     // barrier at its end (whose fence waits for the wave's DMA) publishes both
     // stages.  Past the end of the list the last tile is used again (loads stay
     // unconditional; the extra S is discarded).
-    auto tile = [&](int t) { return __builtin_amdgcn_readfirstlane(list[min(t, n - 1)]); };
+    // Lane j of lv holds list entry t0 + j (clamped to the last entry), so a
+    // step takes its tile indices with v_readlane instead of an LDS round trip
+    // on its critical path; the window moves once every 60 steps or so.
+    int t0 = 0;
+    int lv = list[min(lane, n - 1)];
+    auto tile = [&](int t) { return __builtin_amdgcn_readlane(lv, t - t0); };
     // only the last block of the sequence can be ragged, and it is always the
     // last entry of an ascending list
     kdma(tile(0), 0);
@@ -429,6 +462,10 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
       __syncthreads();
     };
     for (int t = 0; t < n; t += 2) {
+      if (t + 3 - t0 > 63) {      // the two steps below read entries up to t + 3
+        t0 = t;
+        lv = list[min(t0 + lane, n - 1)];
+      }
       body(t, std::integral_constant<int, 0>{});
       if (t + 1 < n) body(t + 1, std::integral_constant<int, 1>{});
     }
