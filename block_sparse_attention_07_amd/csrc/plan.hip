@@ -19,17 +19,51 @@ __global__ void fill_i64_kernel(int64_t* __restrict__ p, int n, int64_t value) {
   if (i < n) p[i] = value;
 }
 
-__global__ void row_counts_kernel(const uint64_t* __restrict__ mask, int n_rows, int nb, int W,
-                                  uint64_t lastmask, int32_t* __restrict__ counts,
-                                  int64_t* __restrict__ head_tiles) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= n_rows) return;
-  const uint64_t* m = mask + (size_t)row * W;
-  int c = 0;
-  for (int w = 0; w < W - 1; ++w) c += __popcll(m[w]);
-  c += __popcll(m[W - 1] & lastmask);
-  counts[row] = c;
-  atomicAdd(reinterpret_cast<unsigned long long*>(head_tiles + row / nb), (unsigned long long)c);
+// One wave per row: lane w reads word w (coalesced), popcounts it, and the wave
+// sums the counts.  Each workgroup adds its rows' counts to the head totals
+// with one atomic per head it touches (rows of a workgroup are consecutive).
+constexpr int RC_THREADS = 256;
+constexpr int RC_ROWS_PER_WAVE = 4;
+constexpr int RC_ROWS = RC_THREADS / 64 * RC_ROWS_PER_WAVE;   // rows per workgroup
+
+__global__ __launch_bounds__(RC_THREADS) void row_counts_kernel(const uint64_t* __restrict__ mask,
+                                                                int n_rows, int nb, int W,
+                                                                uint64_t lastmask,
+                                                                int32_t* __restrict__ counts,
+                                                                int64_t* __restrict__ head_tiles) {
+  __shared__ int wave_sum[RC_ROWS];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * RC_ROWS;
+  for (int k = 0; k < RC_ROWS_PER_WAVE; ++k) {
+    const int slot = wave * RC_ROWS_PER_WAVE + k;
+    const int row = row0 + slot;
+    int c = 0;
+    if (row < n_rows) {
+      const uint64_t* m = mask + (size_t)row * W;
+      for (int w = lane; w < W; w += 64) c += __popcll(w == W - 1 ? (m[w] & lastmask) : m[w]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if (lane == 0) {
+      wave_sum[slot] = c;
+      if (row < n_rows) counts[row] = c;
+    }
+  }
+  __syncthreads();
+  // rows row0 .. row0 + RC_ROWS - 1 belong to heads h_first .. h_last
+  if (threadIdx.x < RC_ROWS) {
+    const int row = row0 + (int)threadIdx.x;
+    if (row < n_rows) {
+      const int h = row / nb;
+      // the first row of each head within this workgroup sums that head's rows
+      if (threadIdx.x == 0 || (row - 1) / nb != h) {
+        int64_t sum = 0;
+        for (int j = threadIdx.x; j < RC_ROWS && row0 + j < n_rows && (row0 + j) / nb == h; ++j) sum += wave_sum[j];
+        atomicAdd(reinterpret_cast<unsigned long long*>(head_tiles + h), (unsigned long long)sum);
+      }
+    }
+  }
 }
 
 // One workgroup per head: rank the head among all heads (more work first, ties
@@ -40,26 +74,31 @@ __global__ void row_counts_kernel(const uint64_t* __restrict__ mask, int n_rows,
 // Within the segment: pairs, then singles, each in decreasing kept-block count
 // (ties by query block), then the -1 slots.
 constexpr int SORT_MAX_NB = 8192;   // rows per head ranked in LDS; longer heads keep u order, no pairs
+constexpr int HO_THREADS = 1024;
 
-__global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restrict__ head_tiles,
-                                                         const int32_t* __restrict__ counts,
-                                                         const uint64_t* __restrict__ mask,
-                                                         int n_heads, int nb, int W, uint64_t lastmask,
-                                                         int32_t* __restrict__ order) {
-  __shared__ int partial[256];
-  __shared__ int key[SORT_MAX_NB];
+__global__ __launch_bounds__(HO_THREADS) void head_order_kernel(const int64_t* __restrict__ head_tiles,
+                                                                const int32_t* __restrict__ counts,
+                                                                const uint64_t* __restrict__ mask,
+                                                                int n_heads, int nb, int W,
+                                                                uint64_t lastmask,
+                                                                int32_t* __restrict__ order) {
+  __shared__ int partial[HO_THREADS / 64];
+  __shared__ uint32_t srt[SORT_MAX_NB];
   __shared__ unsigned char pair[SORT_MAX_NB / 2];
+  const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const int64_t mine = head_tiles[h];
   int before = 0;
-  for (int j = threadIdx.x; j < n_heads; j += blockDim.x) {
+  for (int j = tid; j < n_heads; j += HO_THREADS) {
     const int64_t t = head_tiles[j];
     before += (t > mine) || (t == mine && j < h);
   }
-  partial[threadIdx.x] = before;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) before += __shfl_xor(before, off);
+  if ((tid & 63) == 0) partial[tid >> 6] = before;
   const bool sort_rows = nb <= SORT_MAX_NB;
   if (sort_rows) {
-    for (int i = threadIdx.x; i < nb / 2; i += blockDim.x) {
+    for (int i = tid; i < nb / 2; i += HO_THREADS) {
       const uint64_t* r0 = mask + ((size_t)h * nb + 2 * i) * W;
       const uint64_t* r1 = r0 + W;
       bool eq = true;
@@ -71,32 +110,52 @@ __global__ __launch_bounds__(256) void head_order_kernel(const int64_t* __restri
     }
   }
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) partial[threadIdx.x] += partial[threadIdx.x + s];
-    __syncthreads();
-  }
-  const int rank = partial[0];
+  int rank = 0;
+#pragma unroll
+  for (int i = 0; i < HO_THREADS / 64; ++i) rank += partial[i];
   int32_t* dst = order + (size_t)rank * nb;
   const int total = n_heads * nb;
   if (!sort_rows) {
-    for (int u = threadIdx.x; u < nb; u += blockDim.x) dst[u] = h * nb + u;
+    for (int u = tid; u < nb; u += HO_THREADS) dst[u] = h * nb + u;
     return;
   }
-  // sort key: class (0 pair lead, 1 single, 2 pair follower), then count descending
-  for (int u = threadIdx.x; u < nb; u += blockDim.x) {
-    const bool paired = (u >> 1) < nb / 2 && pair[u >> 1];
-    const int cls = paired ? ((u & 1) ? 2 : 0) : 1;
-    key[u] = (cls << 15) + (16383 - counts[(size_t)h * nb + u]);
+  // Sort key: class (0 pair lead, 1 single, 2 pair follower), then count
+  // descending, then u ascending -- one unique 30-bit value per row, sorted
+  // ascending by a bitonic network over the next power of two (padding sorts
+  // last).
+  int P = 1;
+  while (P < nb) P <<= 1;
+  for (int u = tid; u < P; u += HO_THREADS) {
+    uint32_t v = 0xFFFFFFFFu;
+    if (u < nb) {
+      const bool paired = (u >> 1) < nb / 2 && pair[u >> 1];
+      const uint32_t cls = paired ? ((u & 1) ? 2u : 0u) : 1u;
+      const uint32_t key = (cls << 15) + (16383u - (uint32_t)counts[(size_t)h * nb + u]);
+      v = (key << 13) | (uint32_t)u;
+    }
+    srt[u] = v;
   }
   __syncthreads();
-  for (int u = threadIdx.x; u < nb; u += blockDim.x) {
-    const int ku = key[u];
-    int r = 0;
-    for (int j = 0; j < nb; ++j) {
-      const int kj = key[j];
-      r += (kj < ku) || (kj == ku && j < u);
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += HO_THREADS) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t a = srt[i], b = srt[l];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            srt[i] = b;
+            srt[l] = a;
+          }
+        }
+      }
+      __syncthreads();
     }
-    const int cls = ku >> 15;
+  }
+  for (int r = tid; r < nb; r += HO_THREADS) {
+    const uint32_t v = srt[r];
+    const int u = (int)(v & 8191u);
+    const uint32_t cls = v >> 28;
     dst[r] = cls == 0 ? total + h * nb + u : (cls == 1 ? h * nb + u : -1);
   }
 }
@@ -113,11 +172,11 @@ int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts,
   hipLaunchKernelGGL(fill_i64_kernel, dim3((n_heads + 255) / 256), dim3(256), 0, stream, head_tiles,
                      n_heads, (int64_t)0);
   BSA_CHECK_HIP(hipGetLastError());
-  hipLaunchKernelGGL(row_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, mask, rows,
-                     nb, W, lastmask, counts, head_tiles);
+  hipLaunchKernelGGL(row_counts_kernel, dim3((rows + RC_ROWS - 1) / RC_ROWS), dim3(RC_THREADS), 0, stream,
+                     mask, rows, nb, W, lastmask, counts, head_tiles);
   BSA_CHECK_HIP(hipGetLastError());
-  hipLaunchKernelGGL(head_order_kernel, dim3(n_heads), dim3(256), 0, stream, head_tiles, counts, mask,
-                     n_heads, nb, W, lastmask, order);
+  hipLaunchKernelGGL(head_order_kernel, dim3(n_heads), dim3(HO_THREADS), 0, stream, head_tiles, counts,
+                     mask, n_heads, nb, W, lastmask, order);
   BSA_CHECK_HIP(hipGetLastError());
   return ok();
 }
