@@ -11,10 +11,11 @@
 // own (Cody-Waite reduction with a two-part ln 2, degree-7 Taylor polynomial in
 // Horner form, 2^n assembled from exponent bits, 0 below -87).
 //
-// One workgroup per score row: the row is held in registers (E values per lane),
-// bitonic-sorted by (score descending, index ascending) mostly inside threads and
-// waves, the exponentials are summed and scanned by one lane in sorted order,
-// and the chosen blocks are OR-ed into LDS words.
+// Rows of up to 2048 blocks: one wave per row (topp_wave_kernel), the row held
+// as 64-bit keys in registers and bitonic-sorted inside the wave.  Longer rows:
+// one workgroup per row (topp_kernel), sorted mostly inside threads and waves.
+// Either way the exponentials are summed and scanned by one lane in sorted
+// order and the chosen blocks are OR-ed into LDS words.
 #include <cmath>
 
 #include "bsa_internal.h"
@@ -227,6 +228,183 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
   for (int w = tid; w < W; w += NT) out[w] = words[w];
 }
 
+
+// One wave per row for rows of at most 64 * EW blocks: lane l holds sorted
+// positions EW l .. EW l + EW - 1.  A key is one 64-bit value, the score's bits
+// mapped to an order-preserving unsigned integer (after -0 -> +0, so equal
+// scores stay equal) above the complemented block index, so descending key order
+// is (score descending, index ascending) and every compare-exchange is one
+// 64-bit compare.  Partners less than EW positions apart are exchanged in
+// registers, the others across lanes; the exponentials, the normaliser and the
+// cumulative scan then run exactly as in topp_kernel.  Waves are independent:
+// each has its own LDS region and no workgroup barrier is used.
+constexpr int TW_WAVES = 4;
+
+__device__ __forceinline__ uint32_t ord_bits(float x) {
+  const uint32_t b = __float_as_uint(x + 0.0f);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float ord_float(uint32_t o) {
+  return __uint_as_float(o ^ ((o >> 31) ? 0x80000000u : 0xFFFFFFFFu));
+}
+
+// exchange with lane ^ d (d a power of two below 64), 64 bits
+template <int D>
+__device__ __forceinline__ uint64_t xlane(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint32_t plo, phi;
+  if constexpr (D == 1) {
+    plo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
+    phi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
+  } else if constexpr (D == 2) {
+    plo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
+    phi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
+  } else if constexpr (D < 32) {
+    plo = __builtin_amdgcn_ds_swizzle(lo, 0x1F | (D << 10));
+    phi = __builtin_amdgcn_ds_swizzle(hi, 0x1F | (D << 10));
+  } else {
+    plo = __shfl_xor(lo, 32);
+    phi = __shfl_xor(hi, 32);
+  }
+  return ((uint64_t)phi << 32) | plo;
+}
+
+template <int EW, int D>
+__device__ __forceinline__ void cross_stage(uint64_t (&a)[EW], bool keep_max) {
+#pragma unroll
+  for (int e = 0; e < EW; ++e) {
+    const uint64_t y = xlane<D>(a[e]);
+    const bool take_mine = (a[e] > y) == keep_max;
+    a[e] = take_mine ? a[e] : y;
+  }
+}
+
+template <int EW, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&a)[EW], int lane) {
+  if constexpr (STRIDE < EW) {
+#pragma unroll
+    for (int e = 0; e < EW; ++e) {
+      if ((e & STRIDE) == 0) {
+        const int f = e | STRIDE;
+        // descending inside blocks whose SIZE bit is clear
+        const bool desc = SIZE < EW ? ((e & SIZE) == 0) : (((EW * lane) & SIZE) == 0);
+        const uint64_t x = a[e], y = a[f];
+        const bool sw = (x < y) == desc;
+        a[e] = sw ? y : x;
+        a[f] = sw ? x : y;
+      }
+    }
+  } else {
+    constexpr int D = STRIDE / EW;                    // lane distance
+    const bool lower = (lane & D) == 0;
+    const bool desc = ((EW * lane) & SIZE) == 0;
+    cross_stage<EW, D>(a, lower == desc);
+  }
+  if constexpr (STRIDE > 1) bitonic_stage<EW, SIZE, STRIDE / 2>(a, lane);
+}
+
+template <int EW, int SIZE = 2>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&a)[EW], int lane) {
+  bitonic_stage<EW, SIZE, SIZE / 2>(a, lane);
+  if constexpr (SIZE < 64 * EW) wave_sort_desc<EW, SIZE * 2>(a, lane);
+}
+
+template <int EW>
+__global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* __restrict__ scores,
+                                                                   int n_rows, int nk, int W, float p,
+                                                                   int min_blocks,
+                                                                   uint64_t* __restrict__ mask) {
+#pragma clang fp contract(off)
+  __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][64 * EW];
+  __shared__ unsigned long long words[TW_WAVES][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * TW_WAVES + wv;
+  if (row >= n_rows) return;
+  const float* s = scores + row * (long long)nk;
+  float* b = buf[wv];
+
+  uint64_t a[EW];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < EW; ++e) {
+    const int j = EW * lane + e;
+    if (j < nk) {
+      const float v = s[j];
+      mx = fmaxf(mx, v);
+      a[e] = ((uint64_t)ord_bits(v) << 32) | (uint32_t)~(uint32_t)j;
+    } else {
+      a[e] = 0ull;                                    // sorts after every real key
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const float m = mx;
+  for (int w = lane; w < 64; w += 64) words[wv][w] = 0ull;
+
+  wave_sort_desc<EW>(a, lane);
+
+  // exponentials in sorted order
+#pragma unroll
+  for (int e = 0; e < EW; ++e) {
+    const int r = EW * lane + e;
+    if (r < nk) b[r] = exp_cw(ord_float((uint32_t)(a[e] >> 32)) - m);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the row is in LDS
+  asm volatile("" ::: "memory");
+  float z = 0.0f;
+  if (lane == 0) {
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+    int r = 0;
+#pragma unroll 4
+    for (; r + 4 <= nk; r += 4) {
+      const float4 v = b4[r >> 2];
+      z = z + v.x; z = z + v.y; z = z + v.z; z = z + v.w;
+    }
+    for (; r < nk; ++r) z = z + b[r];
+  }
+  z = __shfl(z, 0);
+#pragma unroll
+  for (int e = 0; e < EW; ++e) {
+    const int r = EW * lane + e;
+    if (r < nk) b[r] = b[r] / z;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  int kk = 0;
+  if (lane == 0) {
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+    float c = 0.0f;
+    int kp = nk;
+    int r = 0;
+    for (; r + 4 <= nk && kp == nk; r += 4) {
+      const float4 v = b4[r >> 2];
+      c = c + v.x; kp = (kp == nk && c >= p) ? r + 1 : kp;
+      c = c + v.y; kp = (kp == nk && c >= p) ? r + 2 : kp;
+      c = c + v.z; kp = (kp == nk && c >= p) ? r + 3 : kp;
+      c = c + v.w; kp = (kp == nk && c >= p) ? r + 4 : kp;
+    }
+    for (; r < nk && kp == nk; ++r) {
+      c = c + b[r];
+      if (c >= p) kp = r + 1;
+    }
+    const int floor_k = min_blocks < nk ? min_blocks : nk;
+    kk = kp > floor_k ? kp : floor_k;
+  }
+  kk = __shfl(kk, 0);
+#pragma unroll
+  for (int e = 0; e < EW; ++e) {
+    const int r = EW * lane + e;
+    if (r < kk) {
+      const uint32_t j = ~(uint32_t)a[e];
+      atomicOr(&words[wv][j >> 6], 1ull << (j & 63));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  uint64_t* out = mask + row * (long long)W;
+  for (int w = lane; w < W; w += 64) out[w] = words[wv][w];
+}
 }  // namespace
 }  // namespace bsa
 
@@ -247,14 +425,19 @@ extern "C" int mask_from_block_scores_topp(const float* scores, int n_heads, int
   if (rows > 0x7fffffffLL) return fail(BSA_ERR_INVALID_ARG, "problem too large");
   const dim3 grid((unsigned)rows), block(NT);
   const int W = n_words(n_k_blocks);
-  if (n_k_blocks <= NT)
-    hipLaunchKernelGGL(topp_kernel<1>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
-  else if (n_k_blocks <= 2 * NT)
-    hipLaunchKernelGGL(topp_kernel<2>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
-  else if (n_k_blocks <= 4 * NT)
-    hipLaunchKernelGGL(topp_kernel<4>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
-  else if (n_k_blocks <= 8 * NT)
-    hipLaunchKernelGGL(topp_kernel<8>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
+  const dim3 wgrid((unsigned)((rows + TW_WAVES - 1) / TW_WAVES)), wblock(64 * TW_WAVES);
+  if (n_k_blocks <= 64)
+    hipLaunchKernelGGL(topp_wave_kernel<1>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 128)
+    hipLaunchKernelGGL(topp_wave_kernel<2>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 256)
+    hipLaunchKernelGGL(topp_wave_kernel<4>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 512)
+    hipLaunchKernelGGL(topp_wave_kernel<8>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 1024)
+    hipLaunchKernelGGL(topp_wave_kernel<16>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 2048)
+    hipLaunchKernelGGL(topp_wave_kernel<32>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
   else
     hipLaunchKernelGGL(topp_kernel<16>, grid, block, 0, stream, scores, n_k_blocks, W, p, min_blocks, mask_bits);
   BSA_CHECK_HIP(hipGetLastError());

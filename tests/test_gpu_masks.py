@@ -43,11 +43,15 @@ def test_stripes_random_tuples_and_odd_frames():
         _stripe_case(params, T, F)
 
 
-@pytest.mark.parametrize("nk", [1, 5, 64, 65, 1182, 2048, 4096])
+@pytest.mark.parametrize("nk", [1, 5, 64, 65, 200, 300, 777, 1182, 2048, 4096])
 def test_topp_bit_exact_random_scores(nk):
+    """Row lengths cover every per-lane width of the one-wave-per-row kernel
+    (1 .. 32 blocks per lane) and the workgroup kernel for longer rows; 51 rows
+    leave a partial last workgroup."""
     s = workloads.random_scores(3, 17, nk, seed=nk)
     s[0, 0] = 0.0                                   # all ties
     s[0, 1] = np.round(s[0, 1])                     # many ties
+    s[2, 3] = np.where(np.arange(nk) % 2 == 0, np.float32(-0.0), np.float32(0.0))   # -0 and +0 are equal
     s[1, 2, nk // 2] = 40.0                         # one dominant block
     sd = gu.to_dev(s)
     for p, mb in [(0.9, 8), (0.5, 0), (0.99, 3), (1.0, 8), (1e-6, 8)]:
