@@ -6,7 +6,7 @@
 //
 // Two kernels.  The pooling pass reads Q and K once, 16 bytes per lane with rows
 // coalesced, and is bound by HBM bandwidth.  The score pass is a small fp32
-// product per head (nb x d times d x nb) tiled 64x64 through LDS.
+// product per head (nb x d times d x nb) on fp32 MFMA, tiled 64x64 through LDS.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -50,51 +50,52 @@ __global__ __launch_bounds__(NT) void pool_kernel(const unsigned short* __restri
 }
 
 // grid (ceil(nb/64), ceil(nb/64), n_heads): one 64x64 output tile per workgroup,
-// 4x4 outputs per thread, the contraction staged 32 dims at a time.
+// each wave a 32x32 quarter on v_mfma_f32_32x32x2_f32 (fp32 products, fp32
+// accumulation).  The tile's qbar and kbar rows are staged in LDS with a row
+// stride of D + 1 floats.  Operand layout (32x32xK MFMA): lane l holds
+// A[l % 32][l / 32] and B[l / 32][l % 32]; result register i of lane l is
+// element (8 (i / 4) + 4 (l / 32) + i % 4, l % 32).
 template <int D>
 __global__ __launch_bounds__(NT) void score_kernel(const float* __restrict__ qbar,
                                                    const float* __restrict__ kbar, int nb,
                                                    float scale, float* __restrict__ S) {
-  __shared__ float qa[32][64 + 1];   // [dim][row]
-  __shared__ float kb[32][64 + 1];   // [dim][col]
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int LD = D + 1;
+  __shared__ float qa[64 * LD];   // [row][dim]
+  __shared__ float kb[64 * LD];
   const int h = blockIdx.z;
   const int u0 = 64 * blockIdx.y, v0 = 64 * blockIdx.x;
   const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
   const float* qh = qbar + (size_t)h * nb * D;
   const float* kh = kbar + (size_t)h * nb * D;
-  float acc[4][4] = {};
-  for (int d0 = 0; d0 < D; d0 += 32) {
-    for (int i = tid; i < 64 * 32; i += NT) {
-      const int r = i >> 5, dd = i & 31;
-      qa[dd][r] = (u0 + r < nb) ? qh[(size_t)(u0 + r) * D + d0 + dd] : 0.f;
-      kb[dd][r] = (v0 + r < nb) ? kh[(size_t)(v0 + r) * D + d0 + dd] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int dd = 0; dd < 32; ++dd) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = qa[dd][ty + 16 * i];
-        b[i] = kb[dd][tx + 16 * i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
+  for (int i = tid; i < 64 * D / 4; i += NT) {
+    const int r = i / (D / 4), c4 = i % (D / 4);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (u0 + r < nb) a = *reinterpret_cast<const float4*>(qh + (size_t)(u0 + r) * D + 4 * c4);
+    if (v0 + r < nb) b = *reinterpret_cast<const float4*>(kh + (size_t)(v0 + r) * D + 4 * c4);
+    float* qd = qa + r * LD + 4 * c4;
+    float* kd = kb + r * LD + 4 * c4;
+    qd[0] = a.x; qd[1] = a.y; qd[2] = a.z; qd[3] = a.w;
+    kd[0] = b.x; kd[1] = b.y; kd[2] = b.z; kd[3] = b.w;
   }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;        // this wave's 32x32 quarter
+  const int l32 = lane & 31, kg = lane >> 5;
+  const float* arow = qa + (32 * wm + l32) * LD + kg;
+  const float* brow = kb + (32 * wn + l32) * LD + kg;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll 16
+  for (int k = 0; k < D; k += 2) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(arow[k], brow[k], acc, 0, 0, 0);
   float* Sh = S + (size_t)h * nb * nb;
+  const int vv = v0 + 32 * wn + l32;
+  if (vv < nb) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int uu = u0 + ty + 16 * i;
-    if (uu >= nb) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int vv = v0 + tx + 16 * j;
-      if (vv < nb) Sh[(size_t)uu * nb + vv] = scale * acc[i][j];
+    for (int i = 0; i < 16; ++i) {
+      const int uu = u0 + 32 * wm + 8 * (i >> 2) + 4 * kg + (i & 3);
+      if (uu < nb) Sh[(size_t)uu * nb + vv] = scale * acc[i];
     }
   }
 }
