@@ -207,6 +207,35 @@ def test_rows_beyond_one_decode_chunk():
         gu.assert_bf16_close(got[h, u * B:u * B + r.shape[0]], r, f"block {u}")
 
 
+def test_long_rows_past_the_planner_sort_limit():
+    """More than 8192 query blocks per head: the planner keeps the rows in block
+    order without pairs (its LDS sort covers 8192 rows), and the attention still
+    matches the oracle; identical adjacent rows are included."""
+    n, d = 64 * 8200 + 5, 64
+    nb = -(-n // B)
+    q, k, v = _rand_bf16(1, n, d, seed=17)
+    rng = np.random.default_rng(17)
+    u = np.arange(nb)
+    keep = (np.abs(u[:, None] - u[None, :]) <= 1)[None].copy()
+    extra = rng.integers(0, nb, size=(nb, 3))
+    keep[0, u[:, None], extra] = True
+    keep[0, 11] = keep[0, 10]                        # identical adjacent rows (no pair here)
+    keep[0, 4000] = False                            # an empty row
+    bits = crm.pack_rows(keep)
+    mdev = gu.to_dev(bits)
+    counts, tiles, order = bsa.plan(mdev, n)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), np.arange(nb))
+    assert np.array_equal(counts.cpu().numpy(), keep[0].sum(1))
+    assert int(tiles.cpu().numpy()[0]) == int(keep.sum())
+    got = _run_bf16(q, k, v, bits, 0.125)
+    blocks = [(0, 0), (0, 10), (0, 11), (0, 4000), (0, nb - 1)] + [(0, int(x)) for x in rng.integers(0, nb, 5)]
+    ref = sparse_attention(_f(q), _f(k), _f(v), bits, 0.125, blocks=blocks)
+    for (h, uu), r in zip(blocks, ref):
+        gu.assert_bf16_close(got[h, uu * B:uu * B + r.shape[0]], r, f"block {uu}")
+    assert np.all(got[0, 4000 * B:4001 * B] == 0.0)
+
+
 @pytest.mark.parametrize("name", ["wan13b_480p", "wan14b_720p"])
 def test_workload_sampled_rows(name):
     w = workloads.WORKLOADS[name]
