@@ -15,8 +15,9 @@ sparse_attn_fwd.  Inputs are resident in HBM before timing starts.
 Reported on one JSON line:
   value      effective TFLOP/s on kept blocks = kept tiles * 4*64*64*128 / step time
   speedup_vs_full_mask   step time with an all-ones mask / step time with the workload mask
-  roofline   the attention kernel alone (planned entry, events on its stream):
-             algorithmic flops per launch / average launch time vs the bf16 MFMA peak
+  roofline   one planned call of the attention path (V transpose, pair launch,
+             single-row slices; events on its stream): algorithmic flops per call /
+             average call time vs the bf16 MFMA peak
   cpu_baseline  the float64 CPU oracle on a bounded sample of query blocks
 
 --sweep  (extra, to stderr) uniform random masks at 5 .. 100 % density on the same
@@ -24,7 +25,7 @@ Reported on one JSON line:
 --aux    (extra, to stderr) the HBM-bound kernels of the path (mask producers,
          block scores, top-p, permutation, resize, fidelity) in GB/s vs 8 TB/s.
 --b128   (extra, to stderr) the same layer under the same mask recipe drawn over
-         128x128-token blocks and passed as 32-bit row words (the pages' format).
+         128x128-token blocks and passed as 32-bit row words (ScalingAttention's CRM format).
 """
 from __future__ import annotations
 
@@ -134,7 +135,7 @@ def density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
 
 
 def b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
-    """The same layer with the mask recipe drawn over the pages' 128-token blocks,
+    """The same layer with the mask recipe drawn over ScalingAttention's 128-token blocks,
     passed as 32-bit row words.  Flops count the kept 64-token tiles of the same
     mask (the expanded form), as the headline metric does."""
     import workloads

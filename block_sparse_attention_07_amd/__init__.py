@@ -4,7 +4,7 @@
 
 computes softmax(scale * Q K^T + M) V where M is 0 on the 64x64 blocks whose bit
 is set in the per-head packed row mask and -inf elsewhere (ScalingAttention,
-section 4.3.2); ``sparse_attn_b128`` takes the pages' own format, 128x128 blocks
+section 4.3.2); ``sparse_attn_b128`` takes ScalingAttention's own format, 128x128 blocks
 in 32-bit words.  Mask producers: ``mask_from_stripes`` (PSA stripe tuples),
 ``block_scores_meanpool`` + ``mask_from_block_scores_topp`` (online top-p with a
 top-k minimum), ``mask_from_threshold_map`` (static masks M = I(T <= p*)) with

@@ -1,4 +1,4 @@
-// The pages' own mask granularity: 128 x 128-token blocks, rows packed in 32-bit
+// ScalingAttention's own mask granularity: 128 x 128-token blocks, rows packed in 32-bit
 // words.
 //
 // ScalingAttention, section 4.3.2: the CRM row mask is an aligned uint32 array,

@@ -55,7 +55,7 @@ const char* bsa_last_error(void);
 
 /* Words per mask row, ceil(ceil(seq_len / block) / 64); -1 if seq_len < 1 or block < 1.
  * ScalingAttention section 4.3.2: one word load decodes as many blocks as the word
- * has bits (the pages' 32-bit words and 128-token blocks give 64 loads per row at
+ * has bits (ScalingAttention's 32-bit words and 128-token blocks give 64 loads per row at
  * 256k tokens; this library's 64-bit words and 64-token blocks give 31 at 126,720). */
 int bsa_mask_words(int seq_len, int block);
 
@@ -132,7 +132,7 @@ int sparse_attn_fwd_planned(const void* q, const void* k, const void* v, const u
                             int block_q, int block_k, float scale, void* out, hipStream_t stream);
 
 /*
- * sparse_attn_fwd_b128 -- sparse_attn_fwd with the pages' own mask format:
+ * sparse_attn_fwd_b128 -- sparse_attn_fwd with ScalingAttention's own mask format:
  * 128 x 128-token blocks, each row packed in 32-bit words (ScalingAttention section
  * 4.3.2: one uint32 load decodes 32 KV blocks; Appendix E, Algorithm 2 steps its
  * base by 32 per word).

@@ -8,7 +8,7 @@ index by the word width per word), reports base + count-trailing-zeros of the
 current word, and clears the lowest set bit to advance.
 
 The pages use 32-bit words with 128-token blocks; the library's main format is
-64-bit words with 64-token blocks, and it also takes the pages' format.  Word
+64-bit words with 64-token blocks, and it also takes ScalingAttention's format.  Word
 ``w`` bit ``b`` (least significant bit = 0) is key block ``word_bits * w + b``;
 bits at positions >= n_blocks are padding and carry no meaning.
 
@@ -62,7 +62,7 @@ def unpack_rows(mask_bits: np.ndarray, n_blocks: int) -> np.ndarray:
 
 
 def unpack_rows32(mask_words: np.ndarray, n_blocks: int) -> np.ndarray:
-    """Decode the pages' 32-bit words [..., n_q, W] into a boolean mask
+    """Decode ScalingAttention's 32-bit words [..., n_q, W] into a boolean mask
     [..., n_q, n_blocks] (bit b of word w is key block 32 w + b)."""
     m = np.ascontiguousarray(mask_words, dtype=np.uint32)
     shifts = np.arange(32, dtype=np.uint32)

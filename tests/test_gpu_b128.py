@@ -1,4 +1,4 @@
-"""GPU parity of the pages' own mask format -- 128 x 128-token blocks in 32-bit
+"""GPU parity of ScalingAttention's own mask format -- 128 x 128-token blocks in 32-bit
 row words -- through the C ABI: the word-for-word expansion is bit-exact, and
 attention over it matches the float64 oracle evaluated at 128-token blocks."""
 import numpy as np

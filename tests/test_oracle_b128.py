@@ -1,4 +1,4 @@
-"""Pins for the pages' own mask granularity: 128-token blocks in 32-bit row-mask
+"""Pins for ScalingAttention's own mask granularity: 128-token blocks in 32-bit row-mask
 words (ScalingAttention, section 4.3.2: one 32-bit load covers 32 KV blocks of
 128 tokens; Appendix E, Algorithm 2 advances its base by the word width)."""
 import math
@@ -58,7 +58,7 @@ def test_32bit_hand_examples_and_packer_roundtrip():
 def test_word_counts_coincide_across_formats():
     """ceil(ceil(N/128)/32) = ceil(N/4096) = ceil(ceil(N/64)/64): a 32-bit row of
     128-token blocks has as many words as a 64-bit row of 64-token blocks; the
-    pages' 256k-token case needs 64."""
+    paper's 256k-token case needs 64."""
     assert crm.words_per_row(262144, 128, 32) == 64
     for n in (1, 64, 128, 4095, 4096, 4097, 32760, 75600, 126720, 262144):
         assert crm.words_per_row(n, 128, 32) == crm.words_per_row(n, 64, 64) == -(-n // 4096)

@@ -27,7 +27,7 @@ def test_iterator_hand_examples():
     assert list(crm.crm_active_blocks([0, 1 << 63])) == [127]
     assert list(crm.crm_active_blocks([0, 0, 0])) == []
     assert list(crm.crm_active_blocks([(1 << 64) - 1])) == list(range(64))
-    # the pages' 32-bit variant: base advances by 32 per word
+    # ScalingAttention's 32-bit variant: base advances by 32 per word
     assert list(crm.crm_active_blocks([0, 0b10], word_bits=32)) == [33]
 
 

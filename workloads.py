@@ -168,7 +168,7 @@ def mask_wan14b(w: Workload, block: int = BLOCK) -> np.ndarray:
     """round(0.2 H) heads full (first entries of a random permutation); every other
     head: band |u-v|<=1 plus random fill to round(rho_h nb^2), rho_h ~ U[0.05, 0.40],
     drawn in head order.  nb = ceil(N / block): 64-token blocks by default, 128 for
-    the pages' own granularity (then the stream is seeded apart)."""
+    ScalingAttention's own granularity (then the stream is seeded apart)."""
     rng = np.random.default_rng([w.seed, 1] if block == BLOCK else [w.seed, 1, block])
     nb = -(-w.seq_len // block)
     full = set(rng.permutation(w.n_heads)[: int(round(0.2 * w.n_heads))].tolist())
