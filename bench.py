@@ -307,7 +307,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": read_traffic(),
-            "kernel": "attn_fwd_bf16_kernel<128, 2> (pair rows) + <128, 1> (single rows), one planned call",
+            "kernel": "attn_pair_kernel<128> (pair rows) + attn_fwd_bf16_kernel<128> (single rows), one planned call",
             "kernel_ms": round(ms_k, 4),
         },
     }

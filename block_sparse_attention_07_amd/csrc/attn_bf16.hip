@@ -5,7 +5,8 @@
 // the set bits of the query block's packed row mask; kept 64x64 tiles are
 // computed densely, all other tiles are skipped without touching their K/V.
 //
-// gfx950 mapping (one workgroup of 4 waves per (head, query block)):
+// gfx950 mapping (one workgroup of 4 waves per (head, query block); two query
+// blocks with identical mask rows share one workgroup, attn_pair_kernel below):
 //  * wave w owns query rows 32*(w&1) .. +31 and key half 32*(w>>1) .. +31 of every
 //    kept tile, so each wave keeps its own running max / sum and output
 //    accumulator; the two key halves are merged once at the end.
@@ -113,12 +114,9 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const u16* __restrict_
   }
 }
 
-// QB = query blocks per workgroup.  QB = 1: one row (64 queries) per
-// workgroup of 4 waves, two workgroups per CU.  QB = 2: two query blocks whose
-// mask rows are identical share every K/V tile; 8 waves, one workgroup per CU
-// (the same waves per SIMD), and each tile is fetched once for 128 queries.
-template <int D, int QB>
-__global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
+// Single rows: one 64-query row per workgroup of 4 waves, two workgroups per CU.
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int wg_offset,
     int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
@@ -143,32 +141,18 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int qb = wave >> 2;         // query block of the pair (0 when QB = 1)
   const int rh = wave & 1;
   const int kh = (wave >> 1) & 1;
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  // Work entries: e in [0, H nb) is the single row e; e in [H nb, 2 H nb) is the
-  // pair of rows e - H nb and e - H nb + 1 (identical mask rows, the first even).
-  // The planner writes each head's entries into the head's segment of nb
-  // slots: pairs first, then singles, then -1.  QB = 1 workgroups run the
-  // singles; QB = 2 workgroup b reads slot b % (nb/2) of segment b / (nb/2).
+  // Work entries: e in [0, H nb) is the single row e; pair entries (>= H nb,
+  // run by attn_pair_kernel) and empty slots (-1) are skipped.
   const int total_rows = n_heads * nb;
-  int row_id;
-  if constexpr (QB == 1) {
-    row_id = wg_offset + blockIdx.x;
-    if (order) {
-      row_id = order[row_id];
-      if (row_id < 0 || row_id >= total_rows) return;
-    }
-  } else {
-    const int half = nb >> 1;
-    const int b = wg_offset + blockIdx.x;
-    const int e = order[(b / half) * nb + (b % half)];
-    if (e < total_rows || e >= 2 * total_rows) return;
-    row_id = e - total_rows;
-    if ((row_id % nb) & 1 || (row_id % nb) + 1 >= nb) return;
+  int row_id = wg_offset + blockIdx.x;
+  if (order) {
+    row_id = order[row_id];
+    if (row_id < 0 || row_id >= total_rows) return;
   }
   const int h = row_id / nb;
   const int u = row_id - h * nb;
@@ -184,7 +168,7 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
   {
     // Rows past the sequence end read the last real row (always in bounds) and
     // are zeroed by a select on the loaded value.
-    const int qrow = BLK * (u + qb) + 32 * rh + r32;
+    const int qrow = BLK * u + 32 * rh + r32;
     const bool qvalid = qrow < N;
     const int qsrc = qvalid ? qrow : N - 1;
 #pragma unroll
@@ -212,7 +196,7 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
   // the chunk the swizzle stores there.  Each wave issues NI instructions per
   // tensor and tile.
   constexpr int KR = 1024 / (2 * D);                  // K rows per DMA instruction
-  constexpr int NI = D / (32 * QB);                    // DMA instructions per wave and tensor
+  constexpr int NI = D / 32;                           // DMA instructions per wave and tensor
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   int k_voff[NI], v_voff[NI];
 #pragma unroll
@@ -362,14 +346,12 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
       if (ks < 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one V operand read
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU ops
     }
-    // Single rows: two workgroups share each SIMD, one wave of each.  Raising
-    // the wave's priority for its PV MFMAs lets them issue back to back while
-    // the other wave runs its VALU-heavy softmax, instead of interleaving both
-    // waves' MFMAs and stretching both steps.
-    if constexpr (QB == 1) {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(2);
-    }
+    // Two workgroups share each SIMD, one wave of each.  Raising the wave's
+    // priority for its PV MFMAs lets them issue back to back while the other
+    // wave runs its VALU-heavy softmax, instead of interleaving both waves'
+    // MFMAs and stretching both steps.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = 32 * db + r32;
@@ -378,10 +360,8 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s0], s0 ? pb1 : pb0, o[db], 0, 0, 0);
       }
     }
-    if constexpr (QB == 1) {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     return sn;
   };
 
@@ -472,18 +452,14 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
   }
 
   // Merge the two key halves of each query-row half and write the output.
-  // mo(j)[accumulator register][lane], j = 2 qb + rh, overlays one tile stage
-  // (each 128 * D bytes): the V^T stages for one query block, also the K
-  // stages for a pair; mm / ml overlay the block list.
+  // mo(j)[accumulator register][lane], j = rh, overlays a V^T stage (each
+  // 128 * D bytes); mm / ml overlay the block list.
   static_assert(sizeof(vts0) == (D / 2) * 64 * sizeof(float), "merge overlay size");
-  static_assert(sizeof(list) >= 2 * 2 * QB * 32 * sizeof(float), "merge overlay size");
-  auto mo = [&](int j) {
-    u16* b = j == 0 ? vts0 : (j == 1 ? vts1 : (j == 2 ? kst0 : kst1));
-    return reinterpret_cast<float (*)[64]>(b);
-  };
-  const int mj = 2 * qb + rh;
+  static_assert(sizeof(list) >= 2 * 2 * 32 * sizeof(float), "merge overlay size");
+  auto mo = [&](int j) { return reinterpret_cast<float (*)[64]>(j ? vts1 : vts0); };
+  const int mj = rh;
   auto mm = reinterpret_cast<float (*)[32]>(list);
-  auto ml = reinterpret_cast<float (*)[32]>(list) + 2 * QB;
+  auto ml = reinterpret_cast<float (*)[32]>(list) + 2;
   __syncthreads();
   const float l_row = l_part + __shfl_xor(l_part, 32);
   if (kh == 1) {
@@ -508,7 +484,7 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
     }
     const float L = l_row * a0 + l1 * a1;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    const int row = BLK * (u + qb) + 32 * rh + r32;
+    const int row = BLK * u + 32 * rh + r32;
     if (row < N) {
       u16* orow = O + head_off + (size_t)row * D;
 #pragma unroll
@@ -527,6 +503,297 @@ __global__ __launch_bounds__(NT * QB, 2 / QB) void attn_fwd_bf16_kernel(
   }
 }
 
+// Pair rows (two query blocks with identical mask rows), four waves: wave w owns
+// the 32 query rows 32 (w & 1) .. +31 of query block u + (w >> 1) against all 64
+// keys of every tile (two QK^T accumulator chains, one per key half, and 16 PV
+// MFMAs).  Both query blocks read the same K/V stages, so each tile is fetched
+// once for 128 queries, and the workgroup is as small as a single-row one: two
+// of them share a CU and each SIMD runs one wave of each, which are not in step.
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int n_heads, int N,
+    int nb, int W, float c, u16* __restrict__ O) {
+  constexpr int CPR = D / 8;
+  constexpr int NDB = D / 32;
+  constexpr int NKS = D / 16;
+  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
+  __shared__ int nlist;
+  auto kstage = [&](int b) { return b ? kst1 : kst0; };
+  auto vstage = [&](int b) { return b ? vts1 : vts0; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qb = wave >> 1;
+  const int rh = wave & 1;
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int total_rows = n_heads * nb;
+  const int half = nb >> 1;
+  const int e = order[(blockIdx.x / half) * nb + (blockIdx.x % half)];
+  if (e < total_rows || e >= 2 * total_rows) return;
+  const int row_id = e - total_rows;
+  if ((row_id % nb) & 1 || (row_id % nb) + 1 >= nb) return;
+  const int h = row_id / nb;
+  const int u = row_id - h * nb;
+  const size_t head_off = (size_t)h * N * D;
+  const u16* Qh = Q + head_off;
+  const u16* Kh = K + head_off;
+  const size_t npad = (size_t)nb * BLK;
+  const u16* VTh = VT + (size_t)h * D * npad;
+  const uint64_t* mrow = mask + ((size_t)h * nb + u) * W;
+
+  bf16x8 qf[NKS];
+  {
+    const int qrow = BLK * (u + qb) + 32 * rh + r32;
+    const bool qvalid = qrow < N;
+    const int qsrc = qvalid ? qrow : N - 1;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 x = *reinterpret_cast<const uint4*>(Qh + (size_t)qsrc * D + 16 * ks + 8 * g);
+      if (!qvalid) x = make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m_run = -1.0e30f;
+  float l_part = 0.f;
+
+  constexpr int KR = 1024 / (2 * D);
+  constexpr int NI = D / 32;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int k_voff[NI], v_voff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int ii = wave_u * NI + i;
+    const int r = ii * KR + lane / CPR;
+    k_voff[i] = (key_of_row(r) * CPR + ((lane % CPR) ^ k_swz<D>(r))) * 16;
+    const int d = 8 * ii + (lane >> 3);
+    v_voff[i] = d * (int)npad * 2 + 16 * ((lane & 7) ^ v_swz(d));
+  }
+  // K operand offsets of key half 0 (rows r32); half 1 is 32 rows further.
+  int k_rd[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) k_rd[ks] = r32 * D * 2 + 16 * ((2 * ks + g) ^ k_swz<D>(r32));
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)((uint32_t)N * D * 2u), BUFFER_DWORD3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(VTh), 0, (int)(D * npad * 2), BUFFER_DWORD3);
+  auto kdma = [&](int kvb, int kbuf) {
+#ifdef __HIP_DEVICE_COMPILE__
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (__attribute__((address_space(3))) void*)(kstage(kbuf) + (wave_u * NI + i) * KR * D), 16,
+          k_voff[i], kvb * BLK * D * 2, 0, 0);
+#endif
+  };
+  auto vdma = [&](int vvb, int vbuf) {
+#ifdef __HIP_DEVICE_COMPILE__
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(vstage(vbuf) + (wave_u * NI + i) * 8 * BLK), 16,
+          v_voff[i], vvb * BLK * 2, 0, 0);
+#endif
+  };
+  auto kread = [&](int kbuf, int kh, int ks) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kstage(kbuf)) + k_rd[ks] +
+                                            kh * 32 * D * 2);
+  };
+  auto qk = [&](int kbuf, int kh) {
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kbuf, kh, ks), qf[ks], s, 0, 0, 0);
+    return s;
+  };
+
+  // One step on tile vb: softmax of S(vb) = (s0, s1) (key halves 0 and 1),
+  // QK^T of the next tile from K stage kbuf (returned in s0n, s1n), PV from V^T
+  // stage vbuf.  Register i of s_kh holds key 32 kh + 16 (i >> 3) + 8 g + (i & 7).
+  auto step = [&](f32x16& s0, f32x16& s1, int vb, int kbuf, int vbuf, bool may_be_ragged) {
+    if (may_be_ragged) {
+      const int hi = N - vb * BLK;
+      if (hi < BLK) {
+        const int kbase = 8 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (kbase >= hi - (16 * (i >> 3) + (i & 7))) s0[i] = -INFINITY;
+          if (kbase >= hi - (32 + 16 * (i >> 3) + (i & 7))) s1[i] = -INFINITY;
+        }
+      }
+    }
+    float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s0[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s1[i]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mt = mx * c;
+    if (__any(mt > m_run + RESCALE_SLACK)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_run = mn;
+    }
+    // key half 0: next tile's QK^T interleaved with this tile's exp2, then half 1
+    bf16x8 pb[2][2];
+    float lsum = 0.f;
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    f32x16 sn[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const f32x16& s = kh ? s1 : s0;
+      bf16x8 ka[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) ka[ks] = kread(kbuf, kh, ks);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[kh][i] = 0.f;
+      float p[16];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sn[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sn[kh], 0, 0, 0);
+        if (2 * ks < 16) {
+          p[2 * ks] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks], c, -m_run));
+          p[2 * ks + 1] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks + 1], c, -m_run));
+        }
+      }
+#pragma unroll
+      for (int i = 2 * NKS; i < 16; i += 2) {
+        p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
+        p[i + 1] = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -m_run));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pb[kh][0][j] = (__bf16)p[j];
+        pb[kh][1][j] = (__bf16)p[8 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[kh][0][2 * j], pb[kh][0][2 * j + 1]}, one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[kh][1][2 * j], pb[kh][1][2 * j + 1]}, one, lsum, false);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
+    l_part += lsum;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {           // k-slot j: keys 16 j .. 16 j + 15
+      const int kh = j >> 1, s0i = j & 1;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + r32;
+        const int chunk = (4 * kh + 2 * s0i + g) ^ v_swz(d);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vstage(vbuf) + d * BLK + 8 * chunk);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][s0i], o[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    s0 = sn[0];
+    s1 = sn[1];
+  };
+
+  const int tail_bits = nb & 63;
+  const uint64_t lastmask = tail_bits ? ((1ull << tail_bits) - 1ull) : ~0ull;
+  const uint64_t lanes_below = (1ull << lane) - 1ull;
+  for (int w0 = 0; w0 < W; w0 += CHUNK_WORDS) {
+    __syncthreads();
+    if (wave == 0) {
+      const int wi = w0 + lane;
+      uint64_t word = 0;
+      if (lane < CHUNK_WORDS && wi < W) {
+        word = mrow[wi];
+        if (wi == W - 1) word &= lastmask;
+      }
+      const int cnt = __popcll(word);
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int b = 0; b < 7; ++b) {
+        const uint64_t bal = __ballot((cnt >> b) & 1);
+        pre += __popcll(bal & lanes_below) << b;
+        tot += __popcll(bal) << b;
+      }
+      const int base = 64 * wi;
+      while (word) {
+        list[pre++] = (u16)(base + __ffsll((unsigned long long)word) - 1);
+        word &= word - 1ull;
+      }
+      if (lane == 0) nlist = tot;
+    }
+    __syncthreads();
+    const int n = nlist;
+    if (n == 0) continue;
+    int t0 = 0;
+    int lv = list[min(lane, n - 1)];
+    auto tile = [&](int t) { return __builtin_amdgcn_readlane(lv, t - t0); };
+    kdma(tile(0), 0);
+    vdma(tile(0), 0);
+    __syncthreads();
+    kdma(tile(1), 1);
+    f32x16 s0 = qk(0, 0), s1 = qk(0, 1);
+    __syncthreads();
+    auto body = [&](int t, auto parity) {
+      constexpr int P = decltype(parity)::value;
+      kdma(tile(t + 2), P);
+      vdma(tile(t + 1), P ^ 1);
+      step(s0, s1, tile(t), P ^ 1, P, t == n - 1);
+      __syncthreads();
+    };
+    for (int t = 0; t < n; t += 2) {
+      if (t + 3 - t0 > 63) {
+        t0 = t;
+        lv = list[min(t0 + lane, n - 1)];
+      }
+      body(t, std::integral_constant<int, 0>{});
+      if (t + 1 < n) body(t + 1, std::integral_constant<int, 1>{});
+    }
+  }
+
+  // Each wave holds whole rows (both key halves): lanes l and l ^ 32 hold the two
+  // key parities of each row's sum.
+  const float l_row = l_part + __shfl_xor(l_part, 32);
+  const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
+  const int row = BLK * (u + qb) + 32 * rh + r32;
+  if (row < N) {
+    u16* orow = O + head_off + (size_t)row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = (__bf16)(o[db][4 * q4 + r] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * q4 + 4 * g) = y;
+      }
+  }
+}
+
 // Workgroups the device holds at once for this kernel (CUs x resident
 // workgroups per CU), cached per device.
 template <int D>
@@ -538,7 +805,7 @@ int generation_size() {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<D, 1>, NT, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_bf16_kernel<D>, NT, 0) != hipSuccess ||
       cus <= 0 || per_cu <= 0)
     return 0;
   cache[dev] = cus * per_cu;
@@ -563,15 +830,15 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   // launch of 128-query workgroups over the pair slots of every head segment.
   const int total = n_heads * nb;
   if (order && nb >= 2) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 2>), dim3((unsigned)(n_heads * (nb / 2))), dim3(2 * NT), 0,
-                       stream, Q, K, VT, mask, order, 0, n_heads, seq_len, nb, W, c, O);
+    hipLaunchKernelGGL((attn_pair_kernel<D>), dim3((unsigned)(n_heads * (nb / 2))), dim3(NT), 0, stream, Q, K,
+                       VT, mask, order, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());
   }
   int gen = order ? generation_size<D>() : 0;
   if (gen <= 0) gen = total;
   for (int off = 0; off < total; off += gen) {
     const int count = min(gen, total - off);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 1>), dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
                        mask, order, off, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());
   }
