@@ -118,8 +118,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const u16* __restrict_
 template <int D>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
-    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int wg_offset,
-    int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int stream_off,
+    int groups, int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
   constexpr int CPR = D / 8;             // 16-byte chunks per token row
   constexpr int NDB = D / 32;            // 32-wide output column blocks
   constexpr int NKS = D / 16;            // k-steps of the QK^T contraction
@@ -148,10 +148,23 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 
   // Work entries: e in [0, H nb) is the single row e; pair entries (>= H nb,
   // run by attn_pair_kernel) and empty slots (-1) are skipped.
+  //
+  // With a work order the rows go out in slices.  The workgroups of a launch
+  // are handed to the 8 XCDs in turn (workgroup i to XCD i mod 8); the XCDs
+  // form `groups` groups (XCD x in group x mod groups), and group g walks its
+  // own stream of slots: the head segments of the heads ranked g, g + groups,
+  // g + 2 groups, ... back to back.  A slice takes gridDim.x / groups
+  // consecutive slots of every stream from stream_off on, so the K/V tiles of
+  // a head are fetched into the L2s of 8 / groups XCDs instead of all eight.
+  // With groups == 1 slot stream_off + blockIdx.x is taken (any grid size).
   const int total_rows = n_heads * nb;
-  int row_id = wg_offset + blockIdx.x;
+  int row_id = blockIdx.x;
   if (order) {
-    row_id = order[row_id];
+    const int i = blockIdx.x, x = i & 7, g = x % groups;
+    const int p = stream_off + x / groups + (8 / groups) * (i >> 3);
+    const int r = g + groups * (p / nb);
+    if (r >= n_heads) return;
+    row_id = order[r * nb + p % nb];
     if (row_id < 0 || row_id >= total_rows) return;
   }
   const int h = row_id / nb;
@@ -824,8 +837,9 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   // length from the same head (the planner groups them) walk their ascending
   // tile lists in step and find each other's K/V tiles in L2; a single launch
   // lets start times drift apart after the first wave of workgroups retires,
-  // and the tiles in use then spread over the whole head.  Without an order
-  // the grid goes out in one launch.
+  // and the tiles in use then spread over the whole head.  Within a slice the
+  // XCDs are split into groups that work on different heads (see the kernel's
+  // row decode).  Without an order the grid goes out in one launch.
   // Pair entries (two query blocks with identical mask rows) go first, in one
   // launch of 128-query workgroups over the pair slots of every head segment.
   const int total = n_heads * nb;
@@ -836,10 +850,24 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   }
   int gen = order ? generation_size<D>() : 0;
   if (gen <= 0) gen = total;
-  for (int off = 0; off < total; off += gen) {
-    const int count = min(gen, total - off);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
-                       mask, order, off, n_heads, seq_len, nb, W, c, O);
+  // XCD groups for the single-row slices: 4 when the heads split evenly over
+  // four streams, else 2 or 1; a slice must be a whole number of rounds of 8.
+  int groups = 1;
+  if (order && gen % 8 == 0) groups = n_heads % 4 == 0 ? 4 : (n_heads % 2 == 0 ? 2 : 1);
+  if (groups == 1) {
+    for (int off = 0; off < total; off += gen) {
+      const int count = min(gen, total - off);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
+                         mask, order, off, 1, n_heads, seq_len, nb, W, c, O);
+      BSA_CHECK_HIP(hipGetLastError());
+    }
+    return ok();
+  }
+  const int per = gen / groups;                 // slots of each stream per slice
+  const int len = (n_heads / groups) * nb;      // slots in each stream
+  for (int off = 0; off < len; off += per) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)gen), dim3(NT), 0, stream, Q, K, VT,
+                       mask, order, off, groups, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());
   }
   return ok();

@@ -207,6 +207,30 @@ def test_rows_beyond_one_decode_chunk():
         gu.assert_bf16_close(got[h, u * B:u * B + r.shape[0]], r, f"block {u}")
 
 
+@pytest.mark.parametrize("H,n,d", [(8, 64 * 70 + 17, 128), (12, 64 * 45, 64), (6, 64 * 90 + 3, 128),
+                                   (5, 64 * 110, 64)])
+def test_every_row_once_across_xcd_groups(H, n, d):
+    """Single rows go out in slices whose XCD groups walk different heads (4
+    groups when H % 4 == 0, else 2 or 1); with more rows than one slice takes,
+    holes from paired rows and an empty row, every row is written once and
+    matches the oracle (the output starts as NaN)."""
+    nb = -(-n // B)
+    q, k, v = _rand_bf16(H, n, d, seed=H * n)
+    rng = np.random.default_rng(H + n)
+    keep = rng.random((H, nb, nb)) < 0.3
+    for h in range(H):
+        for u in range(0, nb - 1, 2):
+            if rng.random() < 0.2:
+                keep[h, u + 1] = keep[h, u]
+    keep[H - 1, 3] = False
+    bits = crm.pack_rows(keep)
+    out = torch.full((H, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    got = _run_bf16(q, k, v, bits, 1.0 / np.sqrt(d), out=out)
+    ref = sparse_attention(_f(q), _f(k), _f(v), bits, 1.0 / np.sqrt(d))
+    gu.assert_bf16_close(got, ref, f"H={H} n={n} d={d}")
+    assert np.all(got[H - 1, 3 * B:4 * B] == 0.0)
+
+
 def test_long_rows_past_the_planner_sort_limit():
     """More than 8192 query blocks per head: the planner keeps the rows in block
     order without pairs (its LDS sort covers 8192 rows), and the attention still
