@@ -5,39 +5,62 @@
 //   S[h][u][v] = scale * <qbar_u, kbar_v>  (fp32).
 //
 // Two kernels.  The pooling pass reads Q and K once, 16 bytes per lane with rows
-// coalesced, and is bound by HBM bandwidth.  The score pass is a small fp32
-// product per head (nb x d times d x nb) on fp32 MFMA, tiled 64x64 through LDS.
+// coalesced, and is bound by HBM bandwidth; it stores each fp32 mean m as three
+// bf16 numbers, m1 = bf16(m), m2 = bf16(m - m1), m3 = bf16(m - m1 - m2), whose sum
+// is m exactly (8 + 8 + 8 significant bits; every subtraction is exact).  The
+// score pass forms the product per head (nb x d times d x nb) on bf16 MFMA from
+// the six partial products a_i b_j with i + j <= 4, smallest first, with fp32
+// accumulation; the three dropped ones are below 3 * 2^-24 of
+// sum_c |qbar_c kbar_c|, as small as fp32 rounding of the product itself.  (fp32
+// MFMA takes 2.7 times the cycles for the same product.)
 #include "bsa_internal.h"
 
 namespace bsa {
 namespace {
 
 constexpr int NT = 256;
+typedef unsigned short u16;
+
+__device__ __forceinline__ u16 bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (u16)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);   // finite inputs only
+}
 
 // grid (nb, n_heads, 2): z selects Q (0) or K (1).  Threads split a block's rows
 // into row groups; each thread sums 8 consecutive dims over its rows in fp32.
+// Output: split[z][part 0..2][h][u][d] bf16.
 template <int D>
-__global__ __launch_bounds__(NT) void pool_kernel(const unsigned short* __restrict__ q,
-                                                  const unsigned short* __restrict__ k, int N,
-                                                  int nb, float* __restrict__ means) {
+__global__ __launch_bounds__(NT) void pool_kernel(const u16* __restrict__ q, const u16* __restrict__ k,
+                                                  int N, int nb, u16* __restrict__ split) {
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int GROUPS = NT / CPR;      // row groups
+  constexpr int PER = 64 / GROUPS;      // rows per thread in a full block
   __shared__ float part[GROUPS][D + 1];
   const int u = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
-  const unsigned short* x = (which ? k : q) + (size_t)h * N * D;
+  const u16* x = (which ? k : q) + (size_t)h * N * D;
   const int tid = threadIdx.x;
   const int ch = tid % CPR, rg = tid / CPR;
   const int row0 = 64 * u;
   const int rows = min(64, N - row0);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = rg; r < rows; r += GROUPS) {
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)(row0 + r) * D + 8 * ch);
+  auto add = [&](const uint4 v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[2 * j] += __uint_as_float(w[j] << 16);
       acc[2 * j + 1] += __uint_as_float(w[j] & 0xffff0000u);
     }
+  };
+  if (rows == 64) {
+    uint4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      v[i] = *reinterpret_cast<const uint4*>(x + (size_t)(row0 + rg + GROUPS * i) * D + 8 * ch);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) add(v[i]);
+  } else {
+    for (int r = rg; r < rows; r += GROUPS)
+      add(*reinterpret_cast<const uint4*>(x + (size_t)(row0 + r) * D + 8 * ch));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) part[rg][8 * ch + j] = acc[j];
@@ -45,58 +68,104 @@ __global__ __launch_bounds__(NT) void pool_kernel(const unsigned short* __restri
   if (tid < D) {
     float s = 0.f;
     for (int g2 = 0; g2 < GROUPS; ++g2) s += part[g2][tid];
-    means[(((size_t)which * gridDim.y + h) * nb + u) * D + tid] = s / (float)rows;
+    const float m = s / (float)rows;
+    const u16 p1 = bf16_rne(m);
+    const float r1 = m - __uint_as_float((uint32_t)p1 << 16);
+    const u16 p2 = bf16_rne(r1);
+    const u16 p3 = bf16_rne(r1 - __uint_as_float((uint32_t)p2 << 16));
+    const size_t plane = (size_t)gridDim.y * nb * D;
+    u16* dst = split + (size_t)which * 3 * plane + ((size_t)h * nb + u) * D + tid;
+    dst[0] = p1;
+    dst[plane] = p2;
+    dst[2 * plane] = p3;
   }
 }
 
-// grid (ceil(nb/64), ceil(nb/64), n_heads): one 64x64 output tile per workgroup,
-// each wave a 32x32 quarter on v_mfma_f32_32x32x2_f32 (fp32 products, fp32
-// accumulation).  The tile's qbar and kbar rows are staged in LDS with a row
-// stride of D + 1 floats.  Operand layout (32x32xK MFMA): lane l holds
-// A[l % 32][l / 32] and B[l / 32][l % 32]; result register i of lane l is
-// element (8 (i / 4) + 4 (l / 32) + i % 4, l % 32).
+// One 128x128 output tile per workgroup, each wave a 64x64 quarter made of 2 x 2 blocks of 32x32 on
+// v_mfma_f32_32x32x16_bf16.  Operands come straight from global memory (L2)
+// into registers: lane l holds row l % 32 of a block, dims 16 ks + 8 (l / 32)
+// .. +7 for k-step ks, which is the A layout (rows = u) and the B layout
+// (columns = v) alike.  Rows past nb read row nb - 1 and are not stored.
+// Result register i of lane l is element (8 (i / 4) + 4 (l / 32) + i % 4, l % 32)
+// of a 32x32 block.
+// Tiles: a panel is 128 rows u of one head; its nvb = ceil(nb / 128) tiles
+// cover all columns.  Rows of S are nb floats apart, so cache lines straddle
+// tile and row ends; workgroup i runs on XCD i mod 8 (workgroups are handed to
+// the XCDs in turn), and every tile of a panel is given to the same XCD, so
+// both halves of a straddling line meet in one L2 before they are written back.
 template <int D>
-__global__ __launch_bounds__(NT) void score_kernel(const float* __restrict__ qbar,
-                                                   const float* __restrict__ kbar, int nb,
-                                                   float scale, float* __restrict__ S) {
+__global__ __launch_bounds__(NT) void score_kernel(const u16* __restrict__ split, int n_heads, int nb,
+                                                   int nvb, float scale, float* __restrict__ S) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x16 __attribute__((ext_vector_type(16)));
-  constexpr int LD = D + 1;
-  __shared__ float qa[64 * LD];   // [row][dim]
-  __shared__ float kb[64 * LD];
-  const int h = blockIdx.z;
-  const int u0 = 64 * blockIdx.y, v0 = 64 * blockIdx.x;
-  const int tid = threadIdx.x;
-  const float* qh = qbar + (size_t)h * nb * D;
-  const float* kh = kbar + (size_t)h * nb * D;
-  for (int i = tid; i < 64 * D / 4; i += NT) {
-    const int r = i / (D / 4), c4 = i % (D / 4);
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    if (u0 + r < nb) a = *reinterpret_cast<const float4*>(qh + (size_t)(u0 + r) * D + 4 * c4);
-    if (v0 + r < nb) b = *reinterpret_cast<const float4*>(kh + (size_t)(v0 + r) * D + 4 * c4);
-    float* qd = qa + r * LD + 4 * c4;
-    float* kd = kb + r * LD + 4 * c4;
-    qd[0] = a.x; qd[1] = a.y; qd[2] = a.z; qd[3] = a.w;
-    kd[0] = b.x; kd[1] = b.y; kd[2] = b.z; kd[3] = b.w;
+  constexpr int NKS = D / 16;
+  const int k8 = blockIdx.x >> 3;
+  const int panel = 8 * (k8 / nvb) + (blockIdx.x & 7);
+  const int vb = k8 % nvb;
+  const int nub = nvb;                                  // panels per head (square S)
+  if (panel >= n_heads * nub) return;
+  const int h = panel / nub;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int u0 = 128 * (panel - h * nub) + 64 * (wave >> 1);
+  const int v0 = 128 * vb + 64 * (wave & 1);
+  const size_t plane = (size_t)n_heads * nb * D;
+  const u16* qs = split + (size_t)h * nb * D;
+  const u16* ks_ = split + 3 * plane + (size_t)h * nb * D;
+  int ra[2], rb[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    ra[j] = min(u0 + 32 * j + l32, nb - 1) * D + 8 * g;
+    rb[j] = min(v0 + 32 * j + l32, nb - 1) * D + 8 * g;
   }
-  __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;        // this wave's 32x32 quarter
-  const int l32 = lane & 31, kg = lane >> 5;
-  const float* arow = qa + (32 * wm + l32) * LD + kg;
-  const float* brow = kb + (32 * wn + l32) * LD + kg;
-  f32x16 acc;
+  auto ld = [&](const u16* base, int off) { return *reinterpret_cast<const bf16x8*>(base + off); };
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll 16
-  for (int k = 0; k < D; k += 2) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(arow[k], brow[k], acc, 0, 0, 0);
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+  // The operands of k-step ks + 1 are loaded while the MFMAs of k-step ks run.
+  bf16x8 av[2][3][2], bv[2][3][2];
+  auto load = [&](int ks, int buf) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        av[buf][t][j] = ld(qs + t * plane, ra[j] + 16 * ks);
+        bv[buf][t][j] = ld(ks_ + t * plane, rb[j] + 16 * ks);
+      }
+  };
+  // (i, j) with i + j <= 4 (parts numbered from 1), smallest terms first
+  constexpr int PI[6] = {2, 0, 1, 1, 0, 0};
+  constexpr int PJ[6] = {0, 2, 1, 0, 1, 0};
+  load(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < NKS) load(ks + 1, cur ^ 1);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int t = 0; t < 6; ++t)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][PI[t]][a], bv[cur][PJ[t]][b], acc[a][b],
+                                                              0, 0, 0);
+  }
   float* Sh = S + (size_t)h * nb * nb;
-  const int vv = v0 + 32 * wn + l32;
-  if (vv < nb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int uu = u0 + 32 * wm + 8 * (i >> 2) + 4 * kg + (i & 3);
-      if (uu < nb) Sh[(size_t)uu * nb + vv] = scale * acc[i];
-    }
+  for (int b = 0; b < 2; ++b) {
+    const int vv = v0 + 32 * b + l32;
+    if (vv >= nb) continue;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int uu = u0 + 32 * a + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (uu < nb) Sh[(size_t)uu * nb + vv] = scale * acc[a][b][i];
+      }
   }
 }
 
@@ -118,22 +187,24 @@ extern "C" int block_scores_meanpool(const void* q, const void* k, int n_heads, 
   const int nb = n_blocks(seq_len, 64);
   if (n_heads > 65535 || nb > 65535)
     return fail(BSA_ERR_INVALID_ARG, "problem too large");
-  const size_t mean_bytes = (size_t)2 * n_heads * nb * head_dim * sizeof(float);
-  float* means = static_cast<float*>(scratch(mean_bytes, stream));
-  if (!means) return BSA_ERR_HIP;
-  const float* qbar = means;
-  const float* kbar = means + (size_t)n_heads * nb * head_dim;
+  // pooled means as three bf16 parts: [Q, K][part][n_heads][nb][head_dim]
+  const size_t split_bytes = (size_t)6 * n_heads * nb * head_dim * sizeof(unsigned short);
+  auto* split = static_cast<unsigned short*>(scratch(split_bytes, stream));
+  if (!split) return BSA_ERR_HIP;
   const auto* qq = static_cast<const unsigned short*>(q);
   const auto* kk = static_cast<const unsigned short*>(k);
-  const dim3 pgrid(nb, n_heads, 2), sgrid((nb + 63) / 64, (nb + 63) / 64, n_heads);
+  const int nvb = (nb + 127) / 128;
+  if ((long long)8 * nvb * ((n_heads * (long long)nvb + 7) / 8) > 0x7fffffffLL)
+    return fail(BSA_ERR_INVALID_ARG, "problem too large");
+  const dim3 pgrid(nb, n_heads, 2), sgrid(8 * nvb * ((n_heads * nvb + 7) / 8));
   if (head_dim == 128) {
-    hipLaunchKernelGGL(pool_kernel<128>, pgrid, dim3(NT), 0, stream, qq, kk, seq_len, nb, means);
+    hipLaunchKernelGGL(pool_kernel<128>, pgrid, dim3(NT), 0, stream, qq, kk, seq_len, nb, split);
     BSA_CHECK_HIP(hipGetLastError());
-    hipLaunchKernelGGL(score_kernel<128>, sgrid, dim3(NT), 0, stream, qbar, kbar, nb, scale, scores);
+    hipLaunchKernelGGL(score_kernel<128>, sgrid, dim3(NT), 0, stream, split, n_heads, nb, nvb, scale, scores);
   } else {
-    hipLaunchKernelGGL(pool_kernel<64>, pgrid, dim3(NT), 0, stream, qq, kk, seq_len, nb, means);
+    hipLaunchKernelGGL(pool_kernel<64>, pgrid, dim3(NT), 0, stream, qq, kk, seq_len, nb, split);
     BSA_CHECK_HIP(hipGetLastError());
-    hipLaunchKernelGGL(score_kernel<64>, sgrid, dim3(NT), 0, stream, qbar, kbar, nb, scale, scores);
+    hipLaunchKernelGGL(score_kernel<64>, sgrid, dim3(NT), 0, stream, split, n_heads, nb, nvb, scale, scores);
   }
   BSA_CHECK_HIP(hipGetLastError());
   return ok();

@@ -70,8 +70,10 @@ def test_block_scores_within_fp32_bound():
     torch.cuda.synchronize()
     qf, kf = workloads.bf16_to_f32(q).astype(np.float64), workloads.bf16_to_f32(k).astype(np.float64)
     ref = block_scores.block_scores(qf, kf, scale)
-    # fp32 error bound: means carry <= 64 eps relative error, the dot product
-    # <= d eps of sum |qbar||kbar| -- bounded by 4e-5 * scale * sum|qbar_c kbar_c|
+    # error budget, relative to sum_c |qbar_c kbar_c|: the fp32 means (<= 64 eps
+    # each), the three partial products dropped from the exact three-part bf16
+    # split (<= 3 * 2^-24), fp32 accumulation over 48 MFMA steps of 16 products
+    # (<= 64 eps) -- below 1.2e-5 in all, inside the 4e-5 bar
     qb, kb = block_scores.block_means(qf), block_scores.block_means(kf)
     bound = 4e-5 * scale * np.einsum("hud,hvd->huv", np.abs(qb), np.abs(kb)) + 1e-12
     err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
@@ -125,9 +127,23 @@ def test_topp_pipeline_end_to_end():
     print(f"[topp] density {crm.unpack_rows(bits_gpu, w.n_blocks).mean():.4f}, "
           f"rows differing {int((~same).sum())} of {same.size}", flush=True)
     assert (~same).sum() <= max(5, same.size // 1000)
-    for h, u in zip(*np.nonzero(~same)):
-        assert topp.boundary_margin(s_ref[h, u], p, mb) < 1e-4
+    # A row may differ where the float32 cumulative mass passes p within reach of
+    # rounding, or where blocks whose scores are equal within the block-score
+    # tolerance straddle the cut-off (their order is not fixed by fp32-accurate
+    # scores): then both sides keep the same number of blocks.
     keep = crm.unpack_rows(bits_ref, w.n_blocks)
+    keep_gpu = crm.unpack_rows(bits_gpu, w.n_blocks)
+    for h, u in zip(*np.nonzero(~same)):
+        if topp.boundary_margin(s_ref[h, u], p, mb) < 1e-4:
+            continue
+        kr, kg = keep[h, u], keep_gpu[h, u]
+        assert kr.sum() == kg.sum(), (h, u)
+        d = np.nonzero(kr != kg)[0]
+        cut = np.sort(s_ref[h, u])[::-1][int(kr.sum()) - 1]
+        qb = block_scores.block_means(f(qp[h:h + 1]))[0, u]
+        kb = block_scores.block_means(f(kp[h:h + 1]))[0, d]
+        tol = 4e-5 * w.scale * (np.abs(kb) @ np.abs(qb))
+        assert np.all(np.abs(s_ref[h, u, d] - cut) <= tol), (h, u, d)
     blocks = [b for b in gu.sample_blocks(keep, 16, seed=w.seed) if same[b]]
     hs = sorted({h for h, _ in blocks})
     hmap = {h: i for i, h in enumerate(hs)}
