@@ -124,8 +124,12 @@ int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int bl
  * library's per-device scratch buffer (see sparse_attn_fwd about overlapping calls).
  * After the transpose, the pair entries run in one launch, then the single entries as
  * consecutive kernel launches of one device-full of workgroups each (compute units x
- * resident workgroups per unit), in the order given, so that the rows of each slice
- * start together.
+ * resident workgroups per unit), so that the rows of each slice start together.  The
+ * XCDs are split into G groups (G = 4 when n_heads is a multiple of 4, else 2 when it
+ * is even, else 1): group g walks the segments g, g + G, g + 2G, ... back to back, and
+ * each launch takes the next device-full / G slots of every group's walk, so the K/V
+ * tiles of a head are fetched by 8 / G of the 8 XCDs.  Within a segment the order given
+ * is kept.
  */
 int sparse_attn_fwd_planned(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
                             const int32_t* work_order, int n_heads, int seq_len, int head_dim,
