@@ -1,7 +1,7 @@
 """Benchmark: block-sparse attention at the Wan2.1-14B 720p layer shape on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
-                    [--sweep] [--aux] [--b128]
+                    [--sweep] [--aux] [--b128] [--cold]
 
 Workload (synthetic, seeded): 40 heads, head_dim 128, bf16, latent grid
 21x45x80 = 75,600 tokens (1182 blocks of 64); 8 heads keep every block, the
@@ -26,6 +26,8 @@ Reported on one JSON line:
          block scores, top-p, permutation, resize, fidelity) in GB/s vs 8 TB/s.
 --b128   (extra, to stderr) the same layer under the same mask recipe drawn over
          128x128-token blocks and passed as 32-bit row words (ScalingAttention's CRM format).
+--cold   (extra, to stderr) steps timed one by one after a 512 MiB device write that
+         evicts the 256 MB last-level cache (MALL), median against back-to-back steps.
 """
 from __future__ import annotations
 
@@ -198,6 +200,24 @@ def aux_kernels(bsa, torch, timed):
            ms_out.numel() * 8)
 
 
+def cold_steps(torch, fn, stream, n, ms_warm):
+    """Median single-step time after a 512 MiB write that evicts the 256 MB MALL."""
+    junk = torch.empty(1 << 28, dtype=torch.int16, device=stream.device)
+    times = []
+    for _ in range(n):
+        junk.fill_(1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    print(json.dumps({"cold_step_ms": round(times[len(times) // 2], 3), "steps": n,
+                      "warm_step_ms": round(ms_warm, 3)}), file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +230,8 @@ def main():
     ap.add_argument("--aux", action="store_true", help="also time the HBM-bound kernels (stderr)")
     ap.add_argument("--b128", action="store_true",
                     help="also time the layer under a 128x128-block mask in 32-bit words (stderr)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single steps after evicting the last-level cache (stderr)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -317,6 +339,8 @@ def main():
         aux_kernels(bsa, torch, timed)
     if args.b128:
         b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
+    if args.cold:
+        cold_steps(torch, lambda: step(md), stream, max(5, args.steps), ms)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, bits, keep)
     else:
