@@ -124,6 +124,31 @@ __device__ void bitonic_sort(float (&k)[E], int (&ix)[E], float* lk, unsigned sh
   }
 }
 
+// Number of leading values of v[0..n) whose running fp32 sum, added left to
+// right, first reaches p (n if it never does).  The values are non-negative,
+// so the running sum never decreases: a group of four whose last partial sum is
+// below p holds no crossing, and only the group that reaches p is examined term
+// by term.  The additions are the same, in the same order, as one sum per step.
+__device__ __forceinline__ int first_crossing(const float* v, int n, float p) {
+  const float4* v4 = reinterpret_cast<const float4*>(v);
+  float c = 0.0f;
+  int r = 0;
+  for (; r + 4 <= n; r += 4) {
+    const float4 x = v4[r >> 2];
+    const float c1 = c + x.x;
+    const float c2 = c1 + x.y;
+    const float c3 = c2 + x.z;
+    const float c4 = c3 + x.w;
+    if (c4 >= p) return c1 >= p ? r + 1 : (c2 >= p ? r + 2 : (c3 >= p ? r + 3 : r + 4));
+    c = c4;
+  }
+  for (; r < n; ++r) {
+    c = c + v[r];
+    if (c >= p) return r + 1;
+  }
+  return n;
+}
+
 template <int E>
 __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scores, int nk, int W,
                                                   float p, int min_blocks,
@@ -198,22 +223,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
   for (int r = tid; r < nk; r += NT) key[r] = key[r] / z;
   __syncthreads();
   if (tid == 0) {
-    float c = 0.0f;
-    int kp = nk;
-    int r = 0;
-    // kp keeps the first crossing; the loop stops at the end of the group of
-    // four where it happens
-    for (; r + 4 <= nk && kp == nk; r += 4) {
-      const float4 v = key4[r >> 2];
-      c = c + v.x; kp = (kp == nk && c >= p) ? r + 1 : kp;
-      c = c + v.y; kp = (kp == nk && c >= p) ? r + 2 : kp;
-      c = c + v.z; kp = (kp == nk && c >= p) ? r + 3 : kp;
-      c = c + v.w; kp = (kp == nk && c >= p) ? r + 4 : kp;
-    }
-    for (; r < nk && kp == nk; ++r) {
-      c = c + key[r];
-      if (c >= p) kp = r + 1;
-    }
+    const int kp = first_crossing(key, nk, p);
     const int floor_k = min_blocks < nk ? min_blocks : nk;
     k_keep = kp > floor_k ? kp : floor_k;
   }
@@ -373,21 +383,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
   asm volatile("" ::: "memory");
   int kk = 0;
   if (lane == 0) {
-    const float4* b4 = reinterpret_cast<const float4*>(b);
-    float c = 0.0f;
-    int kp = nk;
-    int r = 0;
-    for (; r + 4 <= nk && kp == nk; r += 4) {
-      const float4 v = b4[r >> 2];
-      c = c + v.x; kp = (kp == nk && c >= p) ? r + 1 : kp;
-      c = c + v.y; kp = (kp == nk && c >= p) ? r + 2 : kp;
-      c = c + v.z; kp = (kp == nk && c >= p) ? r + 3 : kp;
-      c = c + v.w; kp = (kp == nk && c >= p) ? r + 4 : kp;
-    }
-    for (; r < nk && kp == nk; ++r) {
-      c = c + b[r];
-      if (c >= p) kp = r + 1;
-    }
+    const int kp = first_crossing(b, nk, p);
     const int floor_k = min_blocks < nk ? min_blocks : nk;
     kk = kp > floor_k ? kp : floor_k;
   }
