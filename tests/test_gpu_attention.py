@@ -71,6 +71,40 @@ def test_bf16_random_masks_all_rows(d, n):
     assert np.all(got[0, :B] == 0.0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [1, 17, 63, 65, 127])
+def test_short_sequences(d, n):
+    """Shorter than one or two blocks: the only or the last block is ragged.  Head 0
+    keeps every block (with two blocks its rows are identical and run as a pair),
+    head 1 keeps nothing, head 2 keeps only the ragged last block in every row."""
+    H = 3
+    nb = -(-n // B)
+    q, k, v = _rand_bf16(H, n, d, seed=7 * n + d)
+    keep = np.ones((H, nb, nb), bool)
+    keep[1] = False
+    keep[2, :, :nb - 1] = False
+    bits = crm.pack_rows(keep)
+    scale = 1.0 / np.sqrt(d)
+    got = _run_bf16(q, k, v, bits, scale)
+    ref = sparse_attention(_f(q), _f(k), _f(v), bits, scale)
+    gu.assert_bf16_close(got, ref, f"d={d} n={n}")
+    assert np.all(got[1] == 0.0)
+
+
+@pytest.mark.parametrize("n", [1, 33])
+def test_fp32_short_sequences(n):
+    rng = np.random.default_rng(n)
+    q, k, v = [rng.standard_normal((2, n, 64)).astype(np.float32) for _ in range(3)]
+    keep = np.ones((2, 1, 1), bool)
+    keep[1] = False
+    bits = crm.pack_rows(keep)
+    out = bsa.sparse_attn(gu.to_dev(q), gu.to_dev(k), gu.to_dev(v), gu.to_dev(bits), 0.125)
+    ref = sparse_attention(q, k, v, bits, 0.125)
+    got = out.cpu().numpy()
+    assert np.max(np.abs(got - ref)) <= gu.F32_MAX_ABS
+    assert np.all(got[1] == 0.0)
+
+
 def test_bf16_sharpened_logits():
     """Peaked softmax (scale x 4, and Q/K with a shared component) exposes a
     wrong running max or a missed rescale that flat logits would hide."""
