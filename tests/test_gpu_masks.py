@@ -43,6 +43,21 @@ def test_stripes_random_tuples_and_odd_frames():
         _stripe_case(params, T, F)
 
 
+def test_stripes_whole_block_frames_and_degenerate_tuples():
+    """Frames of 1, 2, 63, 64 whole blocks (one wave per row, words assembled from
+    the frames they overlap) and 65 blocks (one thread per word); tuples with a
+    zero or negative width keep nothing unless the head is full."""
+    rng = np.random.default_rng(23)
+    params = np.zeros((11, 7), np.int32)
+    for i in range(9):
+        params[i] = (int(i == 0), rng.integers(1, 9), rng.integers(-3, 4), rng.integers(0, 4),
+                     rng.integers(1, 70), rng.integers(-5, 6), rng.integers(0, 9))
+    params[9] = (0, 0, 0, 0, 3, 0, 0)
+    params[10] = (0, 3, 0, 0, -1, 0, 0)
+    for T, F in [(70, 64), (33, 128), (3, 64 * 63), (2, 64 * 64), (2, 64 * 65)]:
+        _stripe_case(params, T, F)
+
+
 @pytest.mark.parametrize("nk", [1, 5, 64, 65, 200, 300, 777, 1182, 2048, 4096])
 def test_topp_bit_exact_random_scores(nk):
     """Row lengths cover every per-lane width of the one-wave-per-row kernel
