@@ -15,9 +15,10 @@
 // gets H = 1.
 //
 // Pass 1: one workgroup per (1024-key chunk, head, group of 16 sampled rows)
-// computes the fp32 logits of its rows against its keys (bf16 inputs, VALU dot
-// products; the sampled Q rows are broadcast from LDS) and reduces (max,
-// Z_keep, Z_drop) per row.  Pass 2: one workgroup per head merges the chunks,
+// computes the logits of its rows against its keys on v_mfma_f32_16x16x32_bf16
+// (the 16 sampled rows are the A operand, held in registers; each 16-key tile
+// of K is the B operand, loaded straight from memory; exact bf16 products,
+// fp32 accumulation) and reduces (max, Z_keep, Z_drop) per row.  Pass 2: one workgroup per head merges the chunks,
 // writes each row's H and the head's Fidelity Score 1 - mean H.
 #include <algorithm>
 #include <cmath>
@@ -44,6 +45,12 @@ __device__ __forceinline__ void merge(float& m, float& zk, float& zd, float m2, 
   m = mn;
 }
 
+// Operand layouts of v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 (l / 16) ..
+// +7] and B[8 (l / 16) .. +7][l % 16]; result register i of lane l is C[4 (l / 16) + i]
+// [l % 16].  Wave w walks keys 256 w .. 256 w + 255 of the chunk in 16-key tiles;
+// each lane keeps (max, Z_keep, Z_drop) for its four rows over its key column,
+// starting from a large finite max so keys past the sequence end (logit -inf)
+// contribute exactly nothing.
 template <int D>
 __global__ __launch_bounds__(NT) void fidelity_partial_kernel(const u16* __restrict__ Q,
                                                               const u16* __restrict__ K,
@@ -51,22 +58,28 @@ __global__ __launch_bounds__(NT) void fidelity_partial_kernel(const u16* __restr
                                                               const int32_t* __restrict__ rows, int N,
                                                               int nb, int W, int n_rows, float c,
                                                               int n_chunks, float* __restrict__ part) {
-  __shared__ float qs[RG][D];
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NKS = D / 32;
   __shared__ uint32_t keepbits[RG];
   __shared__ float red[NT / 64][RG][3];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
   const int chunk = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * RG;
   const int nr = min(RG, n_rows - r0);
   const int32_t* hrows = rows + (size_t)h * n_rows + r0;
 
-  for (int i = tid; i < RG * D; i += NT) {
-    const int r = i / D, cc = i % D;
-    float v = 0.f;
-    if (r < nr) {
-      const int tok = hrows[r];
-      if (tok >= 0 && tok < N) v = bf16_to_f32(Q[((size_t)h * N + tok) * D + cc]) * c;
+  bf16x8 qa[NKS];
+  {
+    const int tok = l16 < nr ? hrows[l16] : -1;
+    const bool ok = tok >= 0 && tok < N;
+    const u16* qr = Q + ((size_t)h * N + (ok ? tok : 0)) * D + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 x = *reinterpret_cast<const uint4*>(qr + 32 * ks);
+      if (!ok) x = make_uint4(0, 0, 0, 0);
+      qa[ks] = __builtin_bit_cast(bf16x8, x);
     }
-    qs[r][cc] = v;
   }
   if (tid < RG) {
     uint32_t bits = 0;
@@ -84,56 +97,62 @@ __global__ __launch_bounds__(NT) void fidelity_partial_kernel(const u16* __restr
   }
   __syncthreads();
 
-  float m[RG], zk[RG], zd[RG];
+  float m[4], zk[4], zd[4];
+  uint32_t kb[4];
 #pragma unroll
-  for (int r = 0; r < RG; ++r) { m[r] = -INFINITY; zk[r] = 0.f; zd[r] = 0.f; }
-  const int jend = min(N, (chunk + 1) * CHUNK);
-  for (int j = chunk * CHUNK + tid; j < jend; j += NT) {
-    const u16* kr = K + ((size_t)h * N + j) * D;
-    float acc[RG];
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -1.0e30f;
+    zk[i] = 0.f;
+    zd[i] = 0.f;
+    kb[i] = keepbits[4 * g4 + i];
+  }
+  const int kbeg = chunk * CHUNK + wave * (CHUNK / 4);
+  const int kend = min(N, kbeg + CHUNK / 4);
+  for (int t0 = kbeg; t0 < kend; t0 += 16) {
+    const int key = t0 + l16;
+    const bool kin = key < N;
+    const u16* kr = K + ((size_t)h * N + (kin ? key : N - 1)) * D + 8 * g4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < RG; ++r) acc[r] = 0.f;
-#pragma unroll 4
-    for (int c0 = 0; c0 < D; c0 += 8) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kr + c0);
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kf = bf16_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-#pragma unroll
-        for (int r = 0; r < RG; ++r) acc[r] = fmaf(qs[r][c0 + e], kf, acc[r]);
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 32 * ks));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kv, acc, 0, 0, 0);
     }
-    const uint32_t b = (uint32_t)((j - chunk * CHUNK) >> 6);
+    const uint32_t b = (uint32_t)((t0 - chunk * CHUNK) >> 6);    // 64-key block within the chunk
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const float s = acc[r];
-      if (s > m[r]) {
-        const float f = m[r] == -INFINITY ? 0.f : exp2f(m[r] - s);
-        zk[r] *= f;
-        zd[r] *= f;
-        m[r] = s;
-      }
-      const float e = exp2f(s - m[r]);
-      if ((keepbits[r] >> b) & 1u) zk[r] += e; else zd[r] += e;
+    for (int i = 0; i < 4; ++i) {
+      const float sv = kin ? acc[i] * c : -INFINITY;
+      const float mn = fmaxf(m[i], sv);
+      const float f = exp2f(m[i] - mn);
+      const float e = exp2f(sv - mn);
+      const bool kept = (kb[i] >> b) & 1u;
+      zk[i] = zk[i] * f + (kept ? e : 0.f);
+      zd[i] = zd[i] * f + (kept ? 0.f : e);
+      m[i] = mn;
     }
   }
-  // Reduce the triples over the workgroup.
+  // Reduce over the 16 lanes that share each row, then over the waves.
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float m2 = __shfl_xor(m[r], off), k2 = __shfl_xor(zk[r], off), d2 = __shfl_xor(zd[r], off);
-      merge(m[r], zk[r], zd[r], m2, k2, d2);
+    for (int off = 8; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m[i], off), k2 = __shfl_xor(zk[i], off), d2 = __shfl_xor(zd[i], off);
+      merge(m[i], zk[i], zd[i], m2, k2, d2);
     }
-    if (lane == 0) { red[wave][r][0] = m[r]; red[wave][r][1] = zk[r]; red[wave][r][2] = zd[r]; }
+    if (l16 == 0) {
+      red[wave][4 * g4 + i][0] = m[i];
+      red[wave][4 * g4 + i][1] = zk[i];
+      red[wave][4 * g4 + i][2] = zd[i];
+    }
   }
   __syncthreads();
   if (tid < nr) {
     float mm = red[0][tid][0], kk = red[0][tid][1], dd = red[0][tid][2];
     for (int wv = 1; wv < NT / 64; ++wv) merge(mm, kk, dd, red[wv][tid][0], red[wv][tid][1], red[wv][tid][2]);
     float* o = part + (((size_t)h * n_rows + r0 + tid) * n_chunks + chunk) * 3;
-    o[0] = mm; o[1] = kk; o[2] = dd;
+    o[0] = mm;
+    o[1] = kk;
+    o[2] = dd;
   }
 }
 
