@@ -17,21 +17,40 @@ namespace {
 
 constexpr int NT = 256;
 
+// A wave owns runs of WPW consecutive mask words: lane j tests key 64 w + j of
+// each word, the WPW loads are issued before the WPW ballots, and lane k then
+// stores word k of the run.
+constexpr int WPW = 8;
+
 __global__ __launch_bounds__(NT) void threshold_kernel(const float* __restrict__ T,
                                                        const float* __restrict__ p_head, int nq,
                                                        int nk, int W, long long words,
                                                        uint64_t* __restrict__ mask) {
   const int lane = threadIdx.x & 63;
+  const long long runs = (words + WPW - 1) / WPW;
   const long long stride = (long long)gridDim.x * (NT / 64);
-  for (long long wid = (long long)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); wid < words; wid += stride) {
-    const long long row = wid / W;
-    const int w = (int)(wid - row * W);
-    const int h = (int)(row / nq);
-    const int v = 64 * w + lane;
-    bool keep = false;
-    if (v < nk) keep = T[(size_t)row * nk + v] <= p_head[h];
-    const uint64_t bits = __ballot(keep);
-    if (lane == 0) mask[wid] = bits;
+  for (long long run = (long long)blockIdx.x * (NT / 64) + (threadIdx.x >> 6); run < runs; run += stride) {
+    const long long w0 = run * WPW;
+    long long row = w0 / W;
+    int w = (int)(w0 - row * W);
+    bool keep[WPW];
+#pragma unroll
+    for (int k = 0; k < WPW; ++k) {
+      const int v = 64 * w + lane;
+      keep[k] = false;
+      if (w0 + k < words && v < nk) keep[k] = T[(size_t)row * nk + v] <= p_head[row / nq];
+      if (++w == W) {
+        w = 0;
+        ++row;
+      }
+    }
+    uint64_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < WPW; ++k) {
+      const uint64_t bits = __ballot(keep[k]);
+      if (lane == k) mine = bits;
+    }
+    if (lane < WPW && w0 + lane < words) mask[w0 + lane] = mine;
   }
 }
 
@@ -52,7 +71,8 @@ extern "C" int mask_from_threshold_map(const float* thresholds, const float* p_h
   const int W = n_words(n_k_blocks);
   const long long words = rows * W;
   const long long waves_per_block = NT / 64;
-  const long long blocks = std::min<long long>((words + waves_per_block - 1) / waves_per_block, 1 << 16);
+  const long long runs = (words + WPW - 1) / WPW;
+  const long long blocks = std::min<long long>((runs + waves_per_block - 1) / waves_per_block, 1 << 16);
   hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, thresholds, p_head,
                      n_q_blocks, n_k_blocks, W, words, mask_bits);
   BSA_CHECK_HIP(hipGetLastError());
