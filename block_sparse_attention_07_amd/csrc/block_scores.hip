@@ -169,6 +169,98 @@ __global__ __launch_bounds__(NT) void score_kernel(const u16* __restrict__ split
   }
 }
 
+// Strip form of the score pass: one workgroup of 8 waves per R consecutive
+// rows u of one head computes all nb columns into LDS, laid out exactly as
+// the rows sit in S, and then writes the strip as one contiguous run (R rows
+// of nb floats), so no cache line of S is written in parts by different
+// workgroups.  Products on v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16]
+// [8 (l / 16) .. +7] (rows u) and B[8 (l / 16) .. +7][l % 16] (columns v); result
+// register i of lane l is C[4 (l / 16) + i][l % 16].  Wave w takes the 16-column
+// tiles w, w + 8, ...; the k-bar parts stream from L2 once per strip.  Workgroup i
+// runs on XCD i mod 8, and all strips of head h go to XCD h mod 8, so a head's
+// k-bar parts (0.9 MB at d = 128, nb = 1182) stay in that XCD's L2.
+constexpr int ST = 512;
+template <int D, int R>
+__global__ __launch_bounds__(ST) void score_strip_kernel(const u16* __restrict__ split, int n_heads, int nb,
+                                                         int n_strips, float scale, float* __restrict__ S) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NKS = D / 32;
+  constexpr int RT = R / 16;
+  extern __shared__ float strip[];            // [R][nb]
+  const int k8 = blockIdx.x >> 3;
+  const int h = 8 * (k8 / n_strips) + (blockIdx.x & 7);
+  if (h >= n_heads) return;
+  const int u0 = R * (k8 % n_strips);
+  const int rows = min(R, nb - u0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const size_t plane = (size_t)n_heads * nb * D;
+  const u16* qs = split + (size_t)h * nb * D;
+  const u16* ks_ = split + 3 * plane + (size_t)h * nb * D;
+  auto ld = [&](const u16* base, size_t off) { return *reinterpret_cast<const bf16x8*>(base + off); };
+  bf16x8 av[RT][NKS][3];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const size_t ro = (size_t)min(u0 + 16 * rt + l16, nb - 1) * D + 8 * g4;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) av[rt][k][t] = ld(qs + t * plane, ro + 32 * k);
+  }
+  // (i, j) with i + j <= 4 (parts numbered from 1), smallest terms first
+  constexpr int PI[6] = {2, 0, 1, 1, 0, 0};
+  constexpr int PJ[6] = {0, 2, 1, 0, 1, 0};
+  const int n_ct = (nb + 15) / 16;
+  // The k-bar parts of the next column tile are loaded while the current one
+  // is multiplied; the row tiles' accumulators alternate inside each product so
+  // that consecutive MFMAs are independent.
+  bf16x8 bv[2][NKS][3];
+  auto load_b = [&](int ct, int buf) {
+    const size_t co = (size_t)min(16 * ct + l16, nb - 1) * D + 8 * g4;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) bv[buf][k][t] = ld(ks_ + t * plane, co + 32 * k);
+  };
+  auto tile = [&](int ct, int buf) {
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NKS; ++k)
+#pragma unroll
+      for (int t = 0; t < 6; ++t)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rt][k][PI[t]], bv[buf][k][PJ[t]], acc[rt], 0, 0, 0);
+    const int v = 16 * ct + l16;
+    if (v < nb) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * g4 + i;
+          if (r < rows) strip[r * nb + v] = scale * acc[rt][i];
+        }
+    }
+  };
+  constexpr int WS = ST / 64;                 // waves per workgroup
+  int ct = wave;
+  if (ct < n_ct) load_b(ct, 0);
+  for (; ct < n_ct; ct += 2 * WS) {
+    if (ct + WS < n_ct) load_b(ct + WS, 1);
+    tile(ct, 0);
+    if (ct + WS >= n_ct) break;
+    if (ct + 2 * WS < n_ct) load_b(ct + 2 * WS, 0);
+    tile(ct + WS, 1);
+  }
+  __syncthreads();
+  float* dst = S + ((size_t)h * nb + u0) * nb;
+  const int n = rows * nb;
+  for (int i = threadIdx.x; i < n; i += ST) dst[i] = strip[i];
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -196,15 +288,36 @@ extern "C" int block_scores_meanpool(const void* q, const void* k, int n_heads, 
   const int nvb = (nb + 127) / 128;
   if ((long long)8 * nvb * ((n_heads * (long long)nvb + 7) / 8) > 0x7fffffffLL)
     return fail(BSA_ERR_INVALID_ARG, "problem too large");
+  // strips of R rows when R rows of scores fit in a workgroup's LDS, else 128x128 tiles
+  int dev = 0, lds_max = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    lds_max = 0;
+  const size_t lds = (size_t)lds_max;
+  const int strip_rows = (size_t)32 * nb * 4 <= lds ? 32 : ((size_t)16 * nb * 4 <= lds ? 16 : 0);
   const dim3 pgrid(nb, n_heads, 2), sgrid(8 * nvb * ((n_heads * nvb + 7) / 8));
   if (head_dim == 128) {
     hipLaunchKernelGGL(pool_kernel<128>, pgrid, dim3(NT), 0, stream, qq, kk, seq_len, nb, split);
     BSA_CHECK_HIP(hipGetLastError());
-    hipLaunchKernelGGL(score_kernel<128>, sgrid, dim3(NT), 0, stream, split, n_heads, nb, nvb, scale, scores);
+    if (strip_rows == 32)
+      hipLaunchKernelGGL((score_strip_kernel<128, 32>), dim3(8u * (unsigned)((nb + 31) / 32) * (unsigned)((n_heads + 7) / 8)),
+                         dim3(ST), (size_t)32 * nb * 4, stream, split, n_heads, nb, (nb + 31) / 32, scale, scores);
+    else if (strip_rows == 16)
+      hipLaunchKernelGGL((score_strip_kernel<128, 16>), dim3(8u * (unsigned)((nb + 15) / 16) * (unsigned)((n_heads + 7) / 8)),
+                         dim3(ST), (size_t)16 * nb * 4, stream, split, n_heads, nb, (nb + 15) / 16, scale, scores);
+    else
+      hipLaunchKernelGGL(score_kernel<128>, sgrid, dim3(NT), 0, stream, split, n_heads, nb, nvb, scale, scores);
   } else {
     hipLaunchKernelGGL(pool_kernel<64>, pgrid, dim3(NT), 0, stream, qq, kk, seq_len, nb, split);
     BSA_CHECK_HIP(hipGetLastError());
-    hipLaunchKernelGGL(score_kernel<64>, sgrid, dim3(NT), 0, stream, split, n_heads, nb, nvb, scale, scores);
+    if (strip_rows == 32)
+      hipLaunchKernelGGL((score_strip_kernel<64, 32>), dim3(8u * (unsigned)((nb + 31) / 32) * (unsigned)((n_heads + 7) / 8)),
+                         dim3(ST), (size_t)32 * nb * 4, stream, split, n_heads, nb, (nb + 31) / 32, scale, scores);
+    else if (strip_rows == 16)
+      hipLaunchKernelGGL((score_strip_kernel<64, 16>), dim3(8u * (unsigned)((nb + 15) / 16) * (unsigned)((n_heads + 7) / 8)),
+                         dim3(ST), (size_t)16 * nb * 4, stream, split, n_heads, nb, (nb + 15) / 16, scale, scores);
+    else
+      hipLaunchKernelGGL(score_kernel<64>, sgrid, dim3(NT), 0, stream, split, n_heads, nb, nvb, scale, scores);
   }
   BSA_CHECK_HIP(hipGetLastError());
   return ok();
