@@ -4,7 +4,7 @@
 //   qbar_u = mean of the real tokens of block u (fp32), same for kbar_v,
 //   S[h][u][v] = scale * <qbar_u, kbar_v>  (fp32).
 //
-// Two kernels.  The pooling pass reads Q and K once, 16 bytes per lane with rows
+// The pooling pass reads Q and K once, 16 bytes per lane with rows
 // coalesced, and is bound by HBM bandwidth; it stores each fp32 mean m as three
 // bf16 numbers, m1 = bf16(m), m2 = bf16(m - m1), m3 = bf16(m - m1 - m2), whose sum
 // is m exactly (8 + 8 + 8 significant bits; every subtraction is exact).  The
@@ -12,7 +12,9 @@
 // the six partial products a_i b_j with i + j <= 4, smallest first, with fp32
 // accumulation; the three dropped ones are below 3 * 2^-24 of
 // sum_c |qbar_c kbar_c|, as small as fp32 rounding of the product itself.  (fp32
-// MFMA takes 2.7 times the cycles for the same product.)
+// MFMA takes 2.7 times the cycles for the same product.)  The score pass runs
+// as strips of 32 (or 16) whole rows through LDS when they fit there, so every
+// strip of S is written as one contiguous run; larger nb use 128 x 128 tiles.
 #include "bsa_internal.h"
 
 namespace bsa {
