@@ -113,6 +113,25 @@ def test_permute_gather_scatter_exact():
     assert np.array_equal(yf.cpu().numpy(), hilbert.permute_rows(xf, perm, inverse=True))
 
 
+@pytest.mark.parametrize("nb,d", [(1300, 128), (1300, 64), (2600, 64)])
+def test_block_scores_strip_and_tile_forms(nb, d):
+    """Row counts whose 32-row strips do not fit in LDS (16-row strips) and whose
+    16-row strips do not either (128 x 128 tiles), against the same bound."""
+    n = 64 * nb - 23
+    rng = np.random.default_rng(nb + d)
+    q = workloads.bf16_bits(rng.standard_normal((1, n, d)).astype(np.float32))
+    k = workloads.bf16_bits(rng.standard_normal((1, n, d)).astype(np.float32))
+    scale = 1.0 / np.sqrt(d)
+    got = bsa.block_scores_meanpool(gu.to_dev(q, True), gu.to_dev(k, True), scale)
+    torch.cuda.synchronize()
+    qf, kf = workloads.bf16_to_f32(q).astype(np.float64), workloads.bf16_to_f32(k).astype(np.float64)
+    ref = block_scores.block_scores(qf, kf, scale)
+    qb, kb = block_scores.block_means(qf), block_scores.block_means(kf)
+    bound = 4e-5 * scale * np.einsum("hud,hvd->huv", np.abs(qb), np.abs(kb)) + 1e-12
+    err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
 def test_topp_pipeline_end_to_end():
     """Hilbert permute -> block scores -> top-p mask -> attention -> unpermute, at
     the Wan2.1-14B 720p shape, against the oracle pipeline."""
