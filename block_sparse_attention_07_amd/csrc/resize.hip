@@ -117,6 +117,44 @@ __global__ __launch_bounds__(NT) void mask_resize_kernel(const uint64_t* __restr
   if (u0 + lane < u1) th[(size_t)(u0 + lane) * Wt] = mine;
 }
 
+// The same rule with the head's whole base map staged in LDS (when it fits):
+// a workgroup takes RS_ITEMS (word column, 64-row chunk) items of one head,
+// lane k holds the row samples of target row u0 + k (taken with v_readlane),
+// and every lookup is an LDS read.
+constexpr int RS_ITEMS = 16;
+
+__global__ __launch_bounds__(NT) void mask_resize_lds_kernel(const uint64_t* __restrict__ base, int nb, int nt,
+                                                             int Wb, int Wt, int items,
+                                                             uint64_t* __restrict__ target) {
+  extern __shared__ uint64_t bm[];             // [nb][Wb], base map of head h
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y;
+  const uint64_t* bh = base + (size_t)h * nb * Wb;
+  for (int i = tid; i < nb * Wb; i += NT) bm[i] = bh[i];
+  __syncthreads();
+  for (int it = wave; it < RS_ITEMS; it += NT / 64) {
+    const int item = blockIdx.x * RS_ITEMS + it;
+    if (item >= items) break;                  // uniform per wave
+    const int w = item % Wt, chunk = item / Wt;
+    const int v = 64 * w + lane;
+    const bool vin = v < nt;
+    const Axis y = axis_samples(vin ? v : 0, nb, nt);
+    const int u0 = chunk * ROWS_PER_WAVE, u1 = min(nt, u0 + ROWS_PER_WAVE);
+    const Axis xs = axis_samples(min(u0 + lane, nt - 1), nb, nt);
+    const int ya = y.a >> 6, yb = y.b >> 6, sa = y.a & 63, sb = y.b & 63;
+    uint64_t mine = 0;
+    for (int k = 0; k < u1 - u0; ++k) {
+      const int xa = __builtin_amdgcn_readlane(xs.a, k), xb = __builtin_amdgcn_readlane(xs.b, k);
+      const uint64_t* r0 = bm + xa * Wb;
+      const uint64_t* r1 = bm + xb * Wb;
+      const bool on = vin && ((((r0[ya] >> sa) | (r0[yb] >> sb) | (r1[ya] >> sa) | (r1[yb] >> sb)) & 1ull));
+      const uint64_t bits = __ballot(on);
+      if (lane == k) mine = bits;
+    }
+    if (u0 + lane < u1) target[((size_t)h * nt + u0 + lane) * Wt + w] = mine;
+  }
+}
+
 constexpr int TR_ROWS = 32;   // target rows per workgroup of the threshold resize
 
 // grid (ceil(nt / NT), ceil(nt / TR_ROWS), n_heads): thread = one column.
@@ -159,6 +197,19 @@ extern "C" int mask_resize(const uint64_t* base_bits, int n_heads, int nb_base, 
   if (rc) return rc;
   const int Wb = n_words(nb_base), Wt = n_words(nb_target);
   const int n_chunks = (nb_target + ROWS_PER_WAVE - 1) / ROWS_PER_WAVE;
+  int dev = 0, lds_max = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    lds_max = 0;
+  const size_t map_bytes = (size_t)nb_base * Wb * sizeof(uint64_t);
+  const long long items = (long long)Wt * n_chunks;
+  if (map_bytes <= (size_t)lds_max && items <= 0x7fffffffLL && n_heads <= 65535) {
+    const unsigned gx = (unsigned)((items + RS_ITEMS - 1) / RS_ITEMS);
+    hipLaunchKernelGGL(mask_resize_lds_kernel, dim3(gx, (unsigned)n_heads), dim3(NT), map_bytes, stream, base_bits,
+                       nb_base, nb_target, Wb, Wt, (int)items, target_bits);
+    BSA_CHECK_HIP(hipGetLastError());
+    return ok();
+  }
   const long long waves = (long long)n_heads * Wt * n_chunks;
   const long long blocks = (waves + NT / 64 - 1) / (NT / 64);
   if (blocks > 0x7fffffffLL) return fail(BSA_ERR_INVALID_ARG, "problem too large");

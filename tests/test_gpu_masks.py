@@ -224,7 +224,7 @@ def test_threshold_workload_map_at_layer_shape():
     _threshold_case(T, p)
 
 
-@pytest.mark.parametrize("nb,nt", [(6, 12), (9, 9), (20, 13), (70, 131), (100, 64), (33, 200)])
+@pytest.mark.parametrize("nb,nt", [(6, 12), (9, 9), (20, 13), (70, 131), (100, 64), (33, 200), (512, 1182), (1500, 700)])
 def test_resize_maps_match_oracle(nb, nt):
     rng = np.random.default_rng(nb * 1000 + nt)
     H = 2
