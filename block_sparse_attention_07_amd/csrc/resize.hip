@@ -9,8 +9,10 @@
 // enters with positive weight iff u n_b is not a multiple of n_t.
 //   * mask_resize: packed region maps; a wave owns one 64-column word of the
 //     target for a run of rows: its column samples come from one division per
-//     lane, its row samples advance by remainder arithmetic, and each row's
-//     word is the ballot of the OR of up to four base bits per lane.
+//     lane, its row samples advance by remainder arithmetic (or, with the
+//     head's base map staged in LDS when it fits, come from one division per
+//     lane and are broadcast with v_readlane), and each row's word is the
+//     ballot of the OR of up to four base bits per lane.
 //   * threshold_map_resize: float32 threshold maps; the conservative
 //     counterpart of the ceiling is the minimum over the positive-weight
 //     samples (NaN ignored), so thresholding and resizing commute.  A thread
