@@ -33,15 +33,22 @@ __global__ __launch_bounds__(NT) void threshold_kernel(const float* __restrict__
     const long long w0 = run * WPW;
     long long row = w0 / W;
     int w = (int)(w0 - row * W);
+    int h = (int)(row / nq);
+    int u = (int)(row - (long long)h * nq);
+    float ph = p_head[h];
     bool keep[WPW];
 #pragma unroll
     for (int k = 0; k < WPW; ++k) {
       const int v = 64 * w + lane;
       keep[k] = false;
-      if (w0 + k < words && v < nk) keep[k] = T[(size_t)row * nk + v] <= p_head[row / nq];
+      if (w0 + k < words && v < nk) keep[k] = T[(size_t)row * nk + v] <= ph;
       if (++w == W) {
         w = 0;
         ++row;
+        if (++u == nq && w0 + k + 1 < words) {
+          u = 0;
+          ph = p_head[++h];
+        }
       }
     }
     uint64_t mine = 0;
