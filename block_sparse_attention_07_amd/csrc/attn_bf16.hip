@@ -32,6 +32,15 @@
 //  * Softmax rescaling is lazy: the running max used for exponentials only moves
 //    when a tile's max exceeds it by more than 8 (a factor 256), which keeps every
 //    probability <= 256 and leaves the result exact up to rounding.
+//  * attn_pair_kernel: wave w owns the 32 query rows 32*(w&1) .. +31 of query block
+//    w>>1 and both key halves of every tile (no merge at the end).  Both kernels
+//    run two workgroups per CU, one wave of each per SIMD, and raise wave
+//    priority for their PV MFMAs so that one wave's MFMAs run while the other
+//    wave on the SIMD works through its softmax.
+//  * With a work order, single rows go out one device-full of workgroups per
+//    launch so that rows of similar length start together and walk their tile
+//    lists in step; within a launch the XCDs are split into groups that walk
+//    different heads (see the row decode in attn_fwd_bf16_kernel).
 #include <cmath>
 #include <type_traits>
 
