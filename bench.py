@@ -1,7 +1,7 @@
 """Benchmark: block-sparse attention at the Wan2.1-14B 720p layer shape on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
-                    [--sweep] [--aux] [--b128] [--cold]
+                    [--sweep] [--aux] [--b128] [--cold] [--ceiling]
 
 Workload (synthetic, seeded): 40 heads, head_dim 128, bf16, latent grid
 21x45x80 = 75,600 tokens (1182 blocks of 64); 8 heads keep every block, the
@@ -28,6 +28,9 @@ Reported on one JSON line:
          128x128-token blocks and passed as 32-bit row words (ScalingAttention's CRM format).
 --cold   (extra, to stderr) steps timed one by one after a 512 MiB device write that
          evicts the 256 MB last-level cache (MALL), median against back-to-back steps.
+--ceiling (extra, to stderr) a reference point for the roofline, not part of the path:
+         a dense bf16 GEMM from the vendor library (torch.matmul) at 8192^3 and 16384^3,
+         and the effective rate of one planned call as a fraction of it.
 """
 from __future__ import annotations
 
@@ -200,6 +203,26 @@ def aux_kernels(bsa, torch, timed):
            ms_out.numel() * 8)
 
 
+def gemm_ceiling(torch, timed, achieved):
+    """A dense bf16 GEMM from the vendor library (context for the roofline only)."""
+    dev = torch.device("cuda", 0)
+    best = 0.0
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        fn = lambda: torch.matmul(a, b, out=c)
+        fn()
+        ms = timed(fn, 10 if n == 8192 else 4)
+        tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+        best = max(best, tf)
+        print(json.dumps({"ceiling": f"vendor bf16 GEMM {n}^3 (torch.matmul)", "ms": round(ms, 3),
+                          "tflops": round(tf, 1)}), file=sys.stderr, flush=True)
+        del a, b, c
+    print(json.dumps({"ceiling_best_tflops": round(best, 1), "planned_call_tflops": round(achieved, 1),
+                      "frac_of_ceiling": round(achieved / best, 3)}), file=sys.stderr, flush=True)
+
+
 def cold_steps(torch, fn, stream, n, ms_warm):
     """Median single-step time after a 512 MiB write that evicts the 256 MB MALL."""
     junk = torch.empty(1 << 28, dtype=torch.int16, device=stream.device)
@@ -232,6 +255,8 @@ def main():
                     help="also time the layer under a 128x128-block mask in 32-bit words (stderr)")
     ap.add_argument("--cold", action="store_true",
                     help="also time single steps after evicting the last-level cache (stderr)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time a vendor-library bf16 GEMM as a practical MFMA ceiling (stderr)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -341,6 +366,8 @@ def main():
         b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
     if args.cold:
         cold_steps(torch, lambda: step(md), stream, max(5, args.steps), ms)
+    if args.ceiling:
+        gemm_ceiling(torch, timed, achieved)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, bits, keep)
     else:
