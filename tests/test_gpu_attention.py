@@ -263,6 +263,13 @@ def test_every_row_once_across_xcd_groups(H, n, d):
     ref = sparse_attention(_f(q), _f(k), _f(v), bits, 1.0 / np.sqrt(d))
     gu.assert_bf16_close(got, ref, f"H={H} n={n} d={d}")
     assert np.all(got[H - 1, 3 * B:4 * B] == 0.0)
+    # a caller's plain permutation of the rows, read through the same XCD groups:
+    # every row written once and matching the oracle (rows the planner paired now
+    # run as single rows, whose sums are ordered differently, so not bit for bit)
+    perm = gu.to_dev(np.random.default_rng(H).permutation(H * nb).astype(np.int32))
+    out2 = torch.full((H, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    got2 = _run_bf16(q, k, v, bits, 1.0 / np.sqrt(d), out=out2, work_order=perm)
+    gu.assert_bf16_close(got2, ref, f"H={H} n={n} d={d} permuted")
 
 
 def test_long_rows_past_the_planner_sort_limit():
