@@ -240,14 +240,18 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
 
 
 // One wave per row for rows of at most 64 * EW blocks: lane l holds sorted
-// positions EW l .. EW l + EW - 1.  A key is one 64-bit value, the score's bits
-// mapped to an order-preserving unsigned integer (after -0 -> +0, so equal
-// scores stay equal) above the complemented block index, so descending key order
-// is (score descending, index ascending) and every compare-exchange is one
-// 64-bit compare.  Partners less than EW positions apart are exchanged in
-// registers, the others across lanes; the exponentials, the normaliser and the
-// cumulative scan then run exactly as in topp_kernel.  Waves are independent:
-// each has its own LDS region and no workgroup barrier is used.
+// positions EW l .. EW l + EW - 1.  A key is the score's bits mapped to an
+// order-preserving unsigned 32-bit integer (after -0 -> +0, so equal scores
+// stay equal); partners less than EW positions apart are exchanged in
+// registers, the others across lanes.  The sort leaves equal scores in no
+// particular order, which changes nothing in the sums: equal scores have equal
+// exponentials, so the normaliser and the cumulative scan (run exactly as in
+// topp_kernel) see the same sequence of values as in (score descending, index
+// ascending) order.  The kept set is that order's first k blocks: every block
+// whose key exceeds the k-th key, and the lowest-index blocks whose key equals
+// it, as many as are still needed (a prefix count over the row in index order).
+// Waves are independent: each has its own LDS region and no workgroup barrier
+// is used.
 constexpr int TW_WAVES = 4;
 
 __device__ __forceinline__ uint32_t ord_bits(float x) {
@@ -279,18 +283,29 @@ __device__ __forceinline__ uint64_t xlane(uint64_t v) {
   return ((uint64_t)phi << 32) | plo;
 }
 
-template <int EW, int D>
-__device__ __forceinline__ void cross_stage(uint64_t (&a)[EW], bool keep_max) {
+// exchange with lane ^ d (d a power of two below 64), 32 bits
+template <int D>
+__device__ __forceinline__ uint32_t xlane32(uint32_t v) {
+  if constexpr (D == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (D == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (D < 32) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (D << 10));
+  else return __shfl_xor(v, 32);
+}
+
+template <int EW, int D, typename KT>
+__device__ __forceinline__ void cross_stage(KT (&a)[EW], bool keep_max) {
 #pragma unroll
   for (int e = 0; e < EW; ++e) {
-    const uint64_t y = xlane<D>(a[e]);
+    KT y;
+    if constexpr (sizeof(KT) == 8) y = xlane<D>(a[e]);
+    else y = xlane32<D>(a[e]);
     const bool take_mine = (a[e] > y) == keep_max;
     a[e] = take_mine ? a[e] : y;
   }
 }
 
-template <int EW, int SIZE, int STRIDE>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&a)[EW], int lane) {
+template <int EW, int SIZE, int STRIDE, typename KT>
+__device__ __forceinline__ void bitonic_stage(KT (&a)[EW], int lane) {
   if constexpr (STRIDE < EW) {
 #pragma unroll
     for (int e = 0; e < EW; ++e) {
@@ -298,7 +313,7 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&a)[EW], int lane) {
         const int f = e | STRIDE;
         // descending inside blocks whose SIZE bit is clear
         const bool desc = SIZE < EW ? ((e & SIZE) == 0) : (((EW * lane) & SIZE) == 0);
-        const uint64_t x = a[e], y = a[f];
+        const KT x = a[e], y = a[f];
         const bool sw = (x < y) == desc;
         a[e] = sw ? y : x;
         a[f] = sw ? x : y;
@@ -313,8 +328,8 @@ __device__ __forceinline__ void bitonic_stage(uint64_t (&a)[EW], int lane) {
   if constexpr (STRIDE > 1) bitonic_stage<EW, SIZE, STRIDE / 2>(a, lane);
 }
 
-template <int EW, int SIZE = 2>
-__device__ __forceinline__ void wave_sort_desc(uint64_t (&a)[EW], int lane) {
+template <int EW, int SIZE = 2, typename KT>
+__device__ __forceinline__ void wave_sort_desc(KT (&a)[EW], int lane) {
   bitonic_stage<EW, SIZE, SIZE / 2>(a, lane);
   if constexpr (SIZE < 64 * EW) wave_sort_desc<EW, SIZE * 2>(a, lane);
 }
@@ -334,7 +349,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
   const float* s = scores + row * (long long)nk;
   float* b = buf[wv];
 
-  uint64_t a[EW];
+  uint32_t a[EW];
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < EW; ++e) {
@@ -342,9 +357,9 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
     if (j < nk) {
       const float v = s[j];
       mx = fmaxf(mx, v);
-      a[e] = ((uint64_t)ord_bits(v) << 32) | (uint32_t)~(uint32_t)j;
+      a[e] = ord_bits(v);
     } else {
-      a[e] = 0ull;                                    // sorts after every real key
+      a[e] = 0u;                                      // sorts after every real key
     }
   }
 #pragma unroll
@@ -358,7 +373,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
 #pragma unroll
   for (int e = 0; e < EW; ++e) {
     const int r = EW * lane + e;
-    if (r < nk) b[r] = exp_cw(ord_float((uint32_t)(a[e] >> 32)) - m);
+    if (r < nk) b[r] = exp_cw(ord_float(a[e]) - m);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the row is in LDS
   asm volatile("" ::: "memory");
@@ -388,13 +403,42 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
     kk = kp > floor_k ? kp : floor_k;
   }
   kk = __shfl(kk, 0);
+  // the kk-th key of the sorted row
+  uint32_t cand = 0u;
+#pragma unroll
+  for (int e = 0; e < EW; ++e) cand = (e == (kk - 1) % EW) ? a[e] : cand;
+  const uint32_t kstar = __shfl(cand, (kk - 1) / EW);
+  // the row again in index order: lane l holds blocks EW l .. EW l + EW - 1
+  uint32_t gt = 0u, eq = 0u;
 #pragma unroll
   for (int e = 0; e < EW; ++e) {
-    const int r = EW * lane + e;
-    if (r < kk) {
-      const uint32_t j = ~(uint32_t)a[e];
-      atomicOr(&words[wv][j >> 6], 1ull << (j & 63));
+    const int j = EW * lane + e;
+    const uint32_t o = j < nk ? ord_bits(s[j]) : 0u;
+    gt |= (uint32_t)(j < nk && o > kstar) << e;
+    eq |= (uint32_t)(j < nk && o == kstar) << e;
+  }
+  int n_gt = __popc(gt), n_eq = __popc(eq);
+  int incl = n_eq;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) n_gt += __shfl_xor(n_gt, off);
+  const int need = kk - n_gt;                         // tied blocks still to keep, lowest index first
+  int before = incl - n_eq;                           // tied blocks in lower lanes
+  uint32_t keep = gt;
+#pragma unroll
+  for (int e = 0; e < EW; ++e) {
+    if ((eq >> e) & 1u) {
+      if (before < need) keep |= 1u << e;
+      ++before;
     }
+  }
+  if (keep) {
+    const int j0 = EW * lane;
+    atomicOr(&words[wv][j0 >> 6], (unsigned long long)keep << (j0 & 63));
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("" ::: "memory");
