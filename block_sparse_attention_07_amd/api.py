@@ -12,6 +12,7 @@ uint32 words).
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 
 import numpy as np
@@ -48,6 +49,19 @@ def _dev(*ts):
     return d
 
 
+def _on_device(fn):
+    """Run fn with the device of its first device-tensor argument current: the
+    library sizes launches and keeps its scratch memory per current device."""
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        for a in (*args, *kwargs.values()):
+            if isinstance(a, torch.Tensor) and a.device.type == "cuda":
+                with torch.cuda.device(a.device):
+                    return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+    return wrapped
+
+
 def _check_mask(mask_bits, H, N):
     nb = -(-N // BLOCK)
     _need(mask_bits.dtype == torch.int64, "mask_bits must be int64 (uint64 words)")
@@ -55,6 +69,7 @@ def _check_mask(mask_bits, H, N):
           f"mask_bits must be [{H}, {nb}, {mask_words(N)}], got {tuple(mask_bits.shape)}")
 
 
+@_on_device
 def sparse_attn(q, k, v, mask_bits, scale=None, out=None, work_order=None):
     """Block-sparse attention (sparse_attn_fwd / sparse_attn_fwd_f32 /
     sparse_attn_fwd_planned).  q, k, v: [H, N, d] bf16 or fp32."""
@@ -100,6 +115,7 @@ def _check_mask32(mask_words, H, N):
           f"mask_words must be [{H}, {nb}, {W}], got {tuple(mask_words.shape)}")
 
 
+@_on_device
 def sparse_attn_b128(q, k, v, mask_words, scale=None, out=None):
     """Block-sparse attention over 128 x 128-token blocks with 32-bit row-mask words
     (sparse_attn_fwd_b128).  q, k, v: bf16 [H, N, d]; mask_words int32
@@ -120,6 +136,7 @@ def sparse_attn_b128(q, k, v, mask_words, scale=None, out=None):
     return out
 
 
+@_on_device
 def mask_b128_to_b64(mask_words, seq_len: int, out=None):
     """32-bit rows over 128-token blocks -> the same mask as 64-bit rows over
     64-token blocks (int64 [H, ceil(N/64), ceil(ceil(N/64)/64)])."""
@@ -136,6 +153,7 @@ def mask_b128_to_b64(mask_words, seq_len: int, out=None):
     return out
 
 
+@_on_device
 def plan(mask_bits, seq_len: int):
     """Tile scheduler (sparse_attn_plan): returns (row_counts int32 [H*nb],
     head_tiles int64 [H], work_order int32 [H*nb])."""
@@ -152,6 +170,7 @@ def plan(mask_bits, seq_len: int):
     return counts, tiles, order
 
 
+@_on_device
 def mask_from_stripes(params, n_frames: int, frame_tokens: int, seq_len: int, out=None):
     """PSA stripe tuples int32 [H, 7] (device) -> int64 mask words [H, nb, W]."""
     _dev(params)
@@ -168,6 +187,7 @@ def mask_from_stripes(params, n_frames: int, frame_tokens: int, seq_len: int, ou
     return out
 
 
+@_on_device
 def block_scores_meanpool(q, k, scale=None, out=None):
     """Mean-pooled block scores fp32 [H, nb, nb] from bf16 q, k [H, N, d]."""
     _dev(q, k)
@@ -184,6 +204,7 @@ def block_scores_meanpool(q, k, scale=None, out=None):
     return out
 
 
+@_on_device
 def mask_from_block_scores_topp(scores, p: float, min_blocks: int, out=None):
     """fp32 scores [H, nq, nk] -> int64 mask words [H, nq, ceil(nk/64)]."""
     _dev(scores)
@@ -198,6 +219,7 @@ def mask_from_block_scores_topp(scores, p: float, min_blocks: int, out=None):
     return out
 
 
+@_on_device
 def mask_from_threshold_map(thresholds, p_head, out=None):
     """fp32 threshold map [H, nq, nk] and fp32 levels [H] (device) -> int64 mask
     words [H, nq, ceil(nk/64)] with bit set where T <= p_head[h]."""
@@ -214,6 +236,7 @@ def mask_from_threshold_map(thresholds, p_head, out=None):
     return out
 
 
+@_on_device
 def mask_resize(mask_bits, nb_base: int, nb_target: int, out=None):
     """Region maps int64 [H, nb_base, ceil(nb_base/64)] -> [H, nb_target, ceil(nb_target/64)]
     (Eq. 7: bilinear interpolation with a ceiling)."""
@@ -229,6 +252,7 @@ def mask_resize(mask_bits, nb_base: int, nb_target: int, out=None):
     return out
 
 
+@_on_device
 def threshold_map_resize(thresholds, nb_target: int, out=None):
     """Threshold maps fp32 [H, nb, nb] -> [H, nb_target, nb_target] (min over the
     positive-weight bilinear samples)."""
@@ -244,6 +268,7 @@ def threshold_map_resize(thresholds, nb_target: int, out=None):
     return out
 
 
+@_on_device
 def attn_fidelity(q, k, mask_bits, rows, scale=None):
     """Hellinger distance per sampled row fp32 [H, R] and Fidelity Score per head fp32
     [H] between dense and sparse attention; rows int32 [H, R] token indices (device)."""
@@ -263,6 +288,7 @@ def attn_fidelity(q, k, mask_bits, rows, scale=None):
     return row_h, head_f
 
 
+@_on_device
 def permute_tokens(x, perm, inverse: bool = False, out=None):
     """Gather (inverse=False) or scatter (inverse=True) token rows of x [H, N, d]."""
     _dev(x, perm)

@@ -25,6 +25,9 @@
  * - seq_len is the real token count; keys at positions >= seq_len in the last
  *   block do not exist (they are excluded, never treated as zero keys).
  *   A query row whose mask row keeps no block produces an output of 0.
+ * - Device pointers and `stream` must belong to the calling thread's current HIP
+ *   device: launch sizes and the library's scratch memory are taken per current
+ *   device.
  * - Every device entry point is stream-ordered and asynchronous: it validates its
  *   arguments on the host, enqueues kernels on `stream` and returns.  Faults of
  *   enqueued kernels surface at the caller's next synchronisation.
