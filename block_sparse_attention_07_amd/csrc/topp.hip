@@ -262,34 +262,36 @@ __device__ __forceinline__ float ord_float(uint32_t o) {
   return __uint_as_float(o ^ ((o >> 31) ? 0x80000000u : 0xFFFFFFFFu));
 }
 
-// exchange with lane ^ d (d a power of two below 64), 64 bits
-template <int D>
-__device__ __forceinline__ uint64_t xlane(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  uint32_t plo, phi;
-  if constexpr (D == 1) {
-    plo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
-    phi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true);
-  } else if constexpr (D == 2) {
-    plo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
-    phi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true);
-  } else if constexpr (D < 32) {
-    plo = __builtin_amdgcn_ds_swizzle(lo, 0x1F | (D << 10));
-    phi = __builtin_amdgcn_ds_swizzle(hi, 0x1F | (D << 10));
-  } else {
-    plo = __shfl_xor(lo, 32);
-    phi = __shfl_xor(hi, 32);
-  }
-  return ((uint64_t)phi << 32) | plo;
-}
-
-// exchange with lane ^ d (d a power of two below 64), 32 bits
+// Exchange with lane ^ D (D a power of two below 64), in registers:
+//  * D = 1, 2: DPP quad permutation;
+//  * D = 4, 8: DPP row shifts; lanes whose D bit is clear take the lane D above,
+//    the others the lane D below, both inside the same 16-lane row;
+//  * D = 16, 32: the permlane swaps, which exchange the two halves of every
+//    32- or 64-lane group.  Called with the same value twice, one result holds
+//    the lane's own value and the other its partner's.
 template <int D>
 __device__ __forceinline__ uint32_t xlane32(uint32_t v) {
-  if constexpr (D == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
-  else if constexpr (D == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
-  else if constexpr (D < 32) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (D << 10));
-  else return __shfl_xor(v, 32);
+  if constexpr (D == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+  } else if constexpr (D == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+  } else if constexpr (D == 4 || D == 8) {
+    const uint32_t up = __builtin_amdgcn_mov_dpp(v, 0x100 + D, 0xF, 0xF, true);   // row_shl: lane + D
+    const uint32_t dn = __builtin_amdgcn_mov_dpp(v, 0x110 + D, 0xF, 0xF, true);   // row_shr: lane - D
+    return (threadIdx.x & D) ? dn : up;
+  } else if constexpr (D == 16) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? sw[0] : sw[1];
+  } else {
+    static_assert(D == 32, "lane distance");
+    const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? sw[0] : sw[1];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ uint64_t xlane(uint64_t v) {
+  return ((uint64_t)xlane32<D>((uint32_t)(v >> 32)) << 32) | xlane32<D>((uint32_t)v);
 }
 
 template <int EW, int D, typename KT>
