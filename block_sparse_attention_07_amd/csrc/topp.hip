@@ -12,7 +12,8 @@
 // Horner form, 2^n assembled from exponent bits, 0 below -87).
 //
 // Rows of up to 2048 blocks: one wave per row (topp_wave_kernel), the row held
-// as 64-bit keys in registers and bitonic-sorted inside the wave.  Longer rows:
+// as 32-bit keys in registers and sorted inside the wave by a bitonic network
+// in mirror form (no comparator needs a direction).  Longer rows:
 // one workgroup per row (topp_kernel), sorted mostly inside threads and waves.
 // Either way the exponentials are summed and scanned by one lane in sorted
 // order and the chosen blocks are OR-ed into LDS words.
@@ -289,50 +290,75 @@ __device__ __forceinline__ uint32_t xlane32(uint32_t v) {
   }
 }
 
+// Value of lane ^ (2D - 1) (D a power of two below 64): the lane mirrored
+// inside its group of 2D lanes.
 template <int D>
-__device__ __forceinline__ uint64_t xlane(uint64_t v) {
-  return ((uint64_t)xlane32<D>((uint32_t)(v >> 32)) << 32) | xlane32<D>((uint32_t)v);
-}
-
-template <int EW, int D, typename KT>
-__device__ __forceinline__ void cross_stage(KT (&a)[EW], bool keep_max) {
-#pragma unroll
-  for (int e = 0; e < EW; ++e) {
-    KT y;
-    if constexpr (sizeof(KT) == 8) y = xlane<D>(a[e]);
-    else y = xlane32<D>(a[e]);
-    const bool take_mine = (a[e] > y) == keep_max;
-    a[e] = take_mine ? a[e] : y;
+__device__ __forceinline__ uint32_t xmirror32(uint32_t v) {
+  if constexpr (D == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);          // quad_perm 1,0,3,2
+  } else if constexpr (D == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, true);          // quad_perm 3,2,1,0
+  } else if constexpr (D == 4) {
+    return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);         // row_half_mirror
+  } else if constexpr (D == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true);         // row_mirror
+  } else if constexpr (D == 16) {
+    return __builtin_amdgcn_mov_dpp(xlane32<16>(v), 0x140, 0xF, 0xF, true);
+  } else {
+    static_assert(D == 32, "lane distance");
+    return __builtin_amdgcn_mov_dpp(xlane32<16>(xlane32<32>(v)), 0x140, 0xF, 0xF, true);
   }
 }
 
-template <int EW, int SIZE, int STRIDE, typename KT>
-__device__ __forceinline__ void bitonic_stage(KT (&a)[EW], int lane) {
-  if constexpr (STRIDE < EW) {
+// Bitonic merge network in mirror form (every comparator puts the larger key at
+// the lower position, so no stage needs a direction): the first stage of the
+// merge of size SIZE pairs position i of each SIZE-block with position
+// SIZE - 1 - i, the following stages pair i with i + STRIDE.  Row element
+// EW * lane + e is a[e] of lane `lane`.
+template <int EW, int SIZE, int STRIDE, bool MIRROR>
+__device__ __forceinline__ void merge_stage(uint32_t (&a)[EW], int lane) {
+  if constexpr (SIZE <= EW && MIRROR) {
 #pragma unroll
-    for (int e = 0; e < EW; ++e) {
+    for (int e = 0; e < EW; ++e)
+      if ((e & (SIZE / 2)) == 0) {
+        const int f = e ^ (SIZE - 1);
+        const uint32_t x = a[e], y = a[f];
+        a[e] = x > y ? x : y;
+        a[f] = x > y ? y : x;
+      }
+  } else if constexpr (STRIDE < EW && !MIRROR) {
+#pragma unroll
+    for (int e = 0; e < EW; ++e)
       if ((e & STRIDE) == 0) {
         const int f = e | STRIDE;
-        // descending inside blocks whose SIZE bit is clear
-        const bool desc = SIZE < EW ? ((e & SIZE) == 0) : (((EW * lane) & SIZE) == 0);
-        const KT x = a[e], y = a[f];
-        const bool sw = (x < y) == desc;
-        a[e] = sw ? y : x;
-        a[f] = sw ? x : y;
+        const uint32_t x = a[e], y = a[f];
+        a[e] = x > y ? x : y;
+        a[f] = x > y ? y : x;
       }
-    }
   } else {
-    constexpr int D = STRIDE / EW;                    // lane distance
+    // across lanes: the partner lane is lane ^ (2D - 1) (mirror) or lane ^ D
+    constexpr int D = MIRROR ? SIZE / (2 * EW) : STRIDE / EW;
     const bool lower = (lane & D) == 0;
-    const bool desc = ((EW * lane) & SIZE) == 0;
-    cross_stage<EW, D>(a, lower == desc);
+    uint32_t y[EW];
+#pragma unroll
+    for (int e = 0; e < EW; ++e) y[e] = MIRROR ? xmirror32<D>(a[EW - 1 - e]) : xlane32<D>(a[e]);
+#pragma unroll
+    for (int e = 0; e < EW; ++e) {
+      const bool take_mine = (a[e] > y[e]) == lower;
+      a[e] = take_mine ? a[e] : y[e];
+    }
   }
-  if constexpr (STRIDE > 1) bitonic_stage<EW, SIZE, STRIDE / 2>(a, lane);
+  if constexpr (MIRROR) {
+    if constexpr (SIZE > 2) merge_stage<EW, SIZE, SIZE / 4, false>(a, lane);
+  } else if constexpr (STRIDE > 1) {
+    merge_stage<EW, SIZE, STRIDE / 2, false>(a, lane);
+  }
 }
 
-template <int EW, int SIZE = 2, typename KT>
-__device__ __forceinline__ void wave_sort_desc(KT (&a)[EW], int lane) {
-  bitonic_stage<EW, SIZE, SIZE / 2>(a, lane);
+// Sorts the 64 * EW keys of a wave in descending order.
+template <int EW, int SIZE = 2>
+__device__ __forceinline__ void wave_sort_desc(uint32_t (&a)[EW], int lane) {
+  merge_stage<EW, SIZE, SIZE / 2, true>(a, lane);
   if constexpr (SIZE < 64 * EW) wave_sort_desc<EW, SIZE * 2>(a, lane);
 }
 
