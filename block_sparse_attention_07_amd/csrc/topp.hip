@@ -11,12 +11,15 @@
 // own (Cody-Waite reduction with a two-part ln 2, degree-7 Taylor polynomial in
 // Horner form, 2^n assembled from exponent bits, 0 below -87).
 //
-// Rows of up to 2048 blocks: one wave per row (topp_wave_kernel), the row held
-// as 32-bit keys in registers and sorted inside the wave by a bitonic network
-// in mirror form (no comparator needs a direction).  Longer rows:
-// one workgroup per row (topp_kernel), sorted mostly inside threads and waves.
-// Either way the exponentials are summed and scanned by one lane in sorted
-// order and the chosen blocks are OR-ed into LDS words.
+// Rows of up to 2048 blocks: one wave per row, the row held as 32-bit keys in
+// registers and sorted inside the wave by a bitonic network in mirror form (no
+// comparator needs a direction); rows of 1025 .. 1536 blocks sort their first
+// 1024 blocks and the rest apart and merge the two (topp_wave2_kernel), which
+// spares most of the padding to 2048.  The mask words are built by ballots from
+// the keys in index order.  Longer rows: one workgroup per row (topp_kernel),
+// sorted mostly inside threads and waves, the chosen blocks OR-ed into LDS
+// words.  Either way the exponentials are summed and scanned by one lane in
+// sorted order.
 #include <cmath>
 
 #include "bsa_internal.h"
@@ -240,19 +243,19 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
 }
 
 
-// One wave per row for rows of at most 64 * EW blocks: lane l holds sorted
-// positions EW l .. EW l + EW - 1.  A key is the score's bits mapped to an
-// order-preserving unsigned 32-bit integer (after -0 -> +0, so equal scores
-// stay equal); partners less than EW positions apart are exchanged in
-// registers, the others across lanes.  The sort leaves equal scores in no
+// One wave per row.  Block j of the row is loaded by lane j % 64 as element
+// j / 64, so the loads are coalesced and that copy of the keys is already laid
+// out as the row's mask words (word w = the bits of element w over the lanes).
+// A key is the score's bits mapped to an order-preserving unsigned 32-bit
+// integer (after -0 -> +0, so equal scores stay equal); rows past the end hold
+// key 0, which sorts after every real key.  The sort leaves equal scores in no
 // particular order, which changes nothing in the sums: equal scores have equal
 // exponentials, so the normaliser and the cumulative scan (run exactly as in
 // topp_kernel) see the same sequence of values as in (score descending, index
 // ascending) order.  The kept set is that order's first k blocks: every block
 // whose key exceeds the k-th key, and the lowest-index blocks whose key equals
-// it, as many as are still needed (a prefix count over the row in index order).
-// Waves are independent: each has its own LDS region and no workgroup barrier
-// is used.
+// it, as many as are still needed.  Waves are independent: each has its own
+// LDS region and no workgroup barrier is used.
 constexpr int TW_WAVES = 4;
 
 __device__ __forceinline__ uint32_t ord_bits(float x) {
@@ -362,49 +365,20 @@ __device__ __forceinline__ void wave_sort_desc(uint32_t (&a)[EW], int lane) {
   if constexpr (SIZE < 64 * EW) wave_sort_desc<EW, SIZE * 2>(a, lane);
 }
 
-template <int EW>
-__global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* __restrict__ scores,
-                                                                   int n_rows, int nk, int W, float p,
-                                                                   int min_blocks,
-                                                                   uint64_t* __restrict__ mask) {
-#pragma clang fp contract(off)
-  __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][64 * EW];
-  __shared__ unsigned long long words[TW_WAVES][64];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const long long row = (long long)blockIdx.x * TW_WAVES + wv;
-  if (row >= n_rows) return;
-  const float* s = scores + row * (long long)nk;
-  float* b = buf[wv];
-
-  uint32_t a[EW];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < EW; ++e) {
-    const int j = EW * lane + e;
-    if (j < nk) {
-      const float v = s[j];
-      mx = fmaxf(mx, v);
-      a[e] = ord_bits(v);
-    } else {
-      a[e] = 0u;                                      // sorts after every real key
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  const float m = mx;
-  for (int w = lane; w < 64; w += 64) words[wv][w] = 0ull;
-
-  wave_sort_desc<EW>(a, lane);
-
-  // exponentials in sorted order
-#pragma unroll
-  for (int e = 0; e < EW; ++e) {
-    const int r = EW * lane + e;
-    if (r < nk) b[r] = exp_cw(ord_float(a[e]) - m);
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the row is in LDS
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0)
   asm volatile("" ::: "memory");
+}
+
+// b holds the row's keys in sorted order (as uint32) at positions 0 .. nk-1.
+// Replaces them by their exponentials, sums those sequentially (lane 0),
+// divides each by the sum, and returns the kept-block count
+// kk = max(first position whose running sum of quotients reaches p, min(min_blocks, nk)).
+__device__ __forceinline__ int topp_count(float* b, int nk, float m, float p, int min_blocks, int lane) {
+#pragma clang fp contract(off)
+  const uint32_t* bu = reinterpret_cast<const uint32_t*>(b);
+  for (int r = lane; r < nk; r += 64) b[r] = exp_cw(ord_float(bu[r]) - m);
+  wave_lds_sync();
   float z = 0.0f;
   if (lane == 0) {
     const float4* b4 = reinterpret_cast<const float4*>(b);
@@ -417,61 +391,180 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
     for (; r < nk; ++r) z = z + b[r];
   }
   z = __shfl(z, 0);
-#pragma unroll
-  for (int e = 0; e < EW; ++e) {
-    const int r = EW * lane + e;
-    if (r < nk) b[r] = b[r] / z;
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
+  for (int r = lane; r < nk; r += 64) b[r] = b[r] / z;
+  wave_lds_sync();
   int kk = 0;
   if (lane == 0) {
     const int kp = first_crossing(b, nk, p);
     const int floor_k = min_blocks < nk ? min_blocks : nk;
     kk = kp > floor_k ? kp : floor_k;
   }
-  kk = __shfl(kk, 0);
-  // the kk-th key of the sorted row
-  uint32_t cand = 0u;
+  return __shfl(kk, 0);
+}
+
+// Writes the row's W mask words (W <= NW).  o[w] is the key of block 64 w + lane,
+// which word w holds in bit `lane`.  Kept: every block whose key exceeds kstar,
+// and the `need` lowest-index blocks whose key equals it.
+template <int NW>
+__device__ __forceinline__ void emit_mask(const uint32_t (&o)[NW], int nk, int W, uint32_t kstar, int need,
+                                          uint64_t* __restrict__ out, int lane) {
+  const uint64_t below = (1ull << lane) - 1ull;
+  int before = 0;                                     // tied blocks at lower indices
+  uint64_t mine = 0;                                  // word `lane` of the row
 #pragma unroll
-  for (int e = 0; e < EW; ++e) cand = (e == (kk - 1) % EW) ? a[e] : cand;
-  const uint32_t kstar = __shfl(cand, (kk - 1) / EW);
-  // the row again in index order: lane l holds blocks EW l .. EW l + EW - 1
-  uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-  for (int e = 0; e < EW; ++e) {
-    const int j = EW * lane + e;
-    const uint32_t o = j < nk ? ord_bits(s[j]) : 0u;
-    gt |= (uint32_t)(j < nk && o > kstar) << e;
-    eq |= (uint32_t)(j < nk && o == kstar) << e;
-  }
-  int n_gt = __popc(gt), n_eq = __popc(eq);
-  int incl = n_eq;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) n_gt += __shfl_xor(n_gt, off);
-  const int need = kk - n_gt;                         // tied blocks still to keep, lowest index first
-  int before = incl - n_eq;                           // tied blocks in lower lanes
-  uint32_t keep = gt;
-#pragma unroll
-  for (int e = 0; e < EW; ++e) {
-    if ((eq >> e) & 1u) {
-      if (before < need) keep |= 1u << e;
-      ++before;
+  for (int w = 0; w < NW; ++w) {
+    if (w < W) {
+      const bool real = 64 * w + lane < nk;
+      const uint64_t gt = __ballot(real && o[w] > kstar);
+      const uint64_t eq = __ballot(real && o[w] == kstar);
+      const bool tk = ((eq >> lane) & 1ull) && before + __popcll(eq & below) < need;
+      const uint64_t word = gt | __ballot(tk);
+      before += __popcll(eq);
+      if (lane == w) mine = word;
     }
   }
-  if (keep) {
-    const int j0 = EW * lane;
-    atomicOr(&words[wv][j0 >> 6], (unsigned long long)keep << (j0 & 63));
+  if (lane < W) out[lane] = mine;
+}
+
+// Rows of at most 64 * EW blocks; the sort leaves sorted position EW l + e in
+// element e of lane l.
+template <int EW>
+__global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* __restrict__ scores,
+                                                                   int n_rows, int nk, int W, float p,
+                                                                   int min_blocks,
+                                                                   uint64_t* __restrict__ mask) {
+  __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][64 * EW];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * TW_WAVES + wv;
+  if (row >= n_rows) return;
+  const float* s = scores + row * (long long)nk;
+  float* b = buf[wv];
+
+  uint32_t a[EW], o[EW];                              // o: the keys in index order
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < EW; ++e) {
+    const int j = 64 * e + lane;
+    o[e] = 0u;
+    if (j < nk) {
+      const float v = s[j];
+      mx = fmaxf(mx, v);
+      o[e] = ord_bits(v);
+    }
+    a[e] = o[e];
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
-  uint64_t* out = mask + row * (long long)W;
-  for (int w = lane; w < W; w += 64) out[w] = words[wv][w];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+
+  wave_sort_desc<EW>(a, lane);
+
+  uint32_t* bu = reinterpret_cast<uint32_t*>(b);
+#pragma unroll
+  for (int e = 0; e < EW; ++e)
+    if (EW * lane + e < nk) bu[EW * lane + e] = a[e];
+  wave_lds_sync();
+  const int kk = topp_count(b, nk, mx, p, min_blocks, lane);
+  // the kk-th key of the sorted row, and how many keys exceed it
+  const int pos = kk - 1;
+  uint32_t cand = 0u;
+#pragma unroll
+  for (int e = 0; e < EW; ++e) cand = (e == pos % EW) ? a[e] : cand;
+  const uint32_t kstar = __shfl(cand, pos / EW);
+  int n_gt = 0;
+#pragma unroll
+  for (int e = 0; e < EW; ++e) n_gt += __popcll(__ballot(a[e] > kstar));
+  emit_mask<EW>(o, nk, W, kstar, kk - n_gt, mask + row * (long long)W, lane);
+}
+
+// Rows of 1025 .. 64 * (16 + EW2) blocks: blocks 0 .. 1023 (part A, 16 per lane)
+// and the rest (part B, EW2 per lane) are sorted separately, part B is spread
+// to 16 per lane through LDS (zero keys after its end), and one merge joins
+// them: position i of A faces position 1023 - i of B (lane ^ 63, element
+// 15 - e), A keeps the larger key and B the smaller, then each part is finished
+// by its own half-cleaners.  Sorted position r is then element r % 16 of lane
+// (r % 1024) / 16 of A for r < 1024 and of B otherwise.
+template <int EW2>
+__global__ __launch_bounds__(64 * TW_WAVES) void topp_wave2_kernel(const float* __restrict__ scores,
+                                                                    int n_rows, int nk, int W, float p,
+                                                                    int min_blocks,
+                                                                    uint64_t* __restrict__ mask) {
+  __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][2048];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * TW_WAVES + wv;
+  if (row >= n_rows) return;
+  const float* s = scores + row * (long long)nk;
+  float* b = buf[wv];
+  uint32_t* bu = reinterpret_cast<uint32_t*>(b);
+
+  uint32_t a[16], c2[EW2];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float v = s[64 * e + lane];                 // blocks 0 .. 1023 all exist
+    mx = fmaxf(mx, v);
+    a[e] = ord_bits(v);
+  }
+#pragma unroll
+  for (int e = 0; e < EW2; ++e) {
+    const int j = 1024 + 64 * e + lane;
+    c2[e] = 0u;
+    if (j < nk) {
+      const float v = s[j];
+      mx = fmaxf(mx, v);
+      c2[e] = ord_bits(v);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+
+  wave_sort_desc<16>(a, lane);
+  wave_sort_desc<EW2>(c2, lane);
+#pragma unroll
+  for (int e = 0; e < EW2; ++e) bu[EW2 * lane + e] = c2[e];
+  wave_lds_sync();
+  uint32_t c[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) c[e] = 16 * lane + e < 64 * EW2 ? bu[16 * lane + e] : 0u;
+  wave_lds_sync();
+  {
+    uint32_t ya[16], yc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      ya[e] = xmirror32<32>(c[15 - e]);
+      yc[e] = xmirror32<32>(a[15 - e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      a[e] = a[e] > ya[e] ? a[e] : ya[e];
+      c[e] = c[e] > yc[e] ? yc[e] : c[e];
+    }
+  }
+  merge_stage<16, 2048, 512, false>(a, lane);
+  merge_stage<16, 2048, 512, false>(c, lane);
+
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    bu[16 * lane + e] = a[e];
+    if (1024 + 16 * lane + e < nk) bu[1024 + 16 * lane + e] = c[e];
+  }
+  wave_lds_sync();
+  const int kk = topp_count(b, nk, mx, p, min_blocks, lane);
+  const int pos = kk - 1;
+  uint32_t cand = 0u;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) cand = (e == pos % 16) ? (pos < 1024 ? a[e] : c[e]) : cand;
+  const uint32_t kstar = __shfl(cand, (pos % 1024) / 16);
+  int n_gt = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) n_gt += __popcll(__ballot(a[e] > kstar)) + __popcll(__ballot(c[e] > kstar));
+  // the keys again in index order (coalesced; keeping them through the sort
+  // costs more registers than the two-part sort leaves)
+  uint32_t o[16 + EW2];
+#pragma unroll
+  for (int w = 0; w < 16 + EW2; ++w) o[w] = 64 * w + lane < nk ? ord_bits(s[64 * w + lane]) : 0u;
+  emit_mask<16 + EW2>(o, nk, W, kstar, kk - n_gt, mask + row * (long long)W, lane);
 }
 }  // namespace
 }  // namespace bsa
@@ -504,6 +597,10 @@ extern "C" int mask_from_block_scores_topp(const float* scores, int n_heads, int
     hipLaunchKernelGGL(topp_wave_kernel<8>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
   else if (n_k_blocks <= 1024)
     hipLaunchKernelGGL(topp_wave_kernel<16>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 1280)
+    hipLaunchKernelGGL(topp_wave2_kernel<4>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
+  else if (n_k_blocks <= 1536)
+    hipLaunchKernelGGL(topp_wave2_kernel<8>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
   else if (n_k_blocks <= 2048)
     hipLaunchKernelGGL(topp_wave_kernel<32>, wgrid, wblock, 0, stream, scores, (int)rows, n_k_blocks, W, p, min_blocks, mask_bits);
   else
