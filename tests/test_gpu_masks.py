@@ -58,11 +58,12 @@ def test_stripes_whole_block_frames_and_degenerate_tuples():
         _stripe_case(params, T, F)
 
 
-@pytest.mark.parametrize("nk", [1, 5, 64, 65, 200, 300, 777, 1182, 2048, 4096])
+@pytest.mark.parametrize("nk", [1, 5, 64, 65, 200, 300, 777, 1025, 1182, 1280, 1281, 1536, 1537, 2048, 4096])
 def test_topp_bit_exact_random_scores(nk):
     """Row lengths cover every per-lane width of the one-wave-per-row kernel
-    (1 .. 32 blocks per lane) and the workgroup kernel for longer rows; 51 rows
-    leave a partial last workgroup."""
+    (1 .. 32 blocks per lane), both widths of the two-part kernel (1025 .. 1280
+    and 1281 .. 1536 blocks, with their edges) and the workgroup kernel for
+    longer rows; 51 rows leave a partial last workgroup."""
     s = workloads.random_scores(3, 17, nk, seed=nk)
     s[0, 0] = 0.0                                   # all ties
     s[0, 1] = np.round(s[0, 1])                     # many ties
