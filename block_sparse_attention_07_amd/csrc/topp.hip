@@ -254,8 +254,10 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
 // topp_kernel) see the same sequence of values as in (score descending, index
 // ascending) order.  The kept set is that order's first k blocks: every block
 // whose key exceeds the k-th key, and the lowest-index blocks whose key equals
-// it, as many as are still needed.  Waves are independent: each has its own
-// LDS region and no workgroup barrier is used.
+// it, as many as are still needed.  Each wave has its own LDS region for its
+// row; the sequential sums of a workgroup's rows run side by side on lanes of
+// one wave (topp_count), between workgroup barriers.  Waves past the last row
+// work on row 0 and write nothing.
 constexpr int TW_WAVES = 4;
 
 __device__ __forceinline__ uint32_t ord_bits(float x) {
@@ -370,36 +372,41 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// b holds the row's keys in sorted order (as uint32) at positions 0 .. nk-1.
-// Replaces them by their exponentials, sums those sequentially (lane 0),
-// divides each by the sum, and returns the kept-block count
-// kk = max(first position whose running sum of quotients reaches p, min(min_blocks, nk)).
-__device__ __forceinline__ int topp_count(float* b, int nk, float m, float p, int min_blocks, int lane) {
+// buf[w] holds row w's keys in sorted order (as uint32) at positions 0 .. nk-1.
+// Each wave turns its row into exponentials; lanes 0 .. TW_WAVES-1 of wave 0
+// then run the sequential sums of all rows side by side.
+template <int NS>
+__device__ __forceinline__ int topp_count(float (*buf)[NS], float* zs, int* ks, int nk, float m, float p,
+                                          int min_blocks, int lane, int wv) {
 #pragma clang fp contract(off)
+  float* b = buf[wv];
   const uint32_t* bu = reinterpret_cast<const uint32_t*>(b);
   for (int r = lane; r < nk; r += 64) b[r] = exp_cw(ord_float(bu[r]) - m);
-  wave_lds_sync();
-  float z = 0.0f;
-  if (lane == 0) {
-    const float4* b4 = reinterpret_cast<const float4*>(b);
+  __syncthreads();
+  if (wv == 0 && lane < TW_WAVES) {
+    const float* bl = buf[lane];
+    const float4* b4 = reinterpret_cast<const float4*>(bl);
+    float z = 0.0f;
     int r = 0;
 #pragma unroll 4
     for (; r + 4 <= nk; r += 4) {
       const float4 v = b4[r >> 2];
       z = z + v.x; z = z + v.y; z = z + v.z; z = z + v.w;
     }
-    for (; r < nk; ++r) z = z + b[r];
+    for (; r < nk; ++r) z = z + bl[r];
+    zs[lane] = z;
   }
-  z = __shfl(z, 0);
+  __syncthreads();
+  const float z = zs[wv];
   for (int r = lane; r < nk; r += 64) b[r] = b[r] / z;
-  wave_lds_sync();
-  int kk = 0;
-  if (lane == 0) {
-    const int kp = first_crossing(b, nk, p);
+  __syncthreads();
+  if (wv == 0 && lane < TW_WAVES) {
+    const int kp = first_crossing(buf[lane], nk, p);
     const int floor_k = min_blocks < nk ? min_blocks : nk;
-    kk = kp > floor_k ? kp : floor_k;
+    ks[lane] = kp > floor_k ? kp : floor_k;
   }
-  return __shfl(kk, 0);
+  __syncthreads();
+  return ks[wv];
 }
 
 // Writes the row's W mask words (W <= NW).  o[w] is the key of block 64 w + lane,
@@ -434,11 +441,13 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
                                                                    int min_blocks,
                                                                    uint64_t* __restrict__ mask) {
   __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][64 * EW];
+  __shared__ float zs[TW_WAVES];
+  __shared__ int ks[TW_WAVES];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const long long row = (long long)blockIdx.x * TW_WAVES + wv;
-  if (row >= n_rows) return;
-  const float* s = scores + row * (long long)nk;
+  const bool valid = row < n_rows;
+  const float* s = scores + (valid ? row : 0ll) * (long long)nk;
   float* b = buf[wv];
 
   uint32_t a[EW], o[EW];                              // o: the keys in index order
@@ -464,7 +473,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
   for (int e = 0; e < EW; ++e)
     if (EW * lane + e < nk) bu[EW * lane + e] = a[e];
   wave_lds_sync();
-  const int kk = topp_count(b, nk, mx, p, min_blocks, lane);
+  const int kk = topp_count(buf, zs, ks, nk, mx, p, min_blocks, lane, wv);
   // the kk-th key of the sorted row, and how many keys exceed it
   const int pos = kk - 1;
   uint32_t cand = 0u;
@@ -474,7 +483,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
   int n_gt = 0;
 #pragma unroll
   for (int e = 0; e < EW; ++e) n_gt += __popcll(__ballot(a[e] > kstar));
-  emit_mask<EW>(o, nk, W, kstar, kk - n_gt, mask + row * (long long)W, lane);
+  if (valid) emit_mask<EW>(o, nk, W, kstar, kk - n_gt, mask + row * (long long)W, lane);
 }
 
 // Rows of 1025 .. 64 * (16 + EW2) blocks: blocks 0 .. 1023 (part A, 16 per lane)
@@ -490,11 +499,13 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave2_kernel(const float* 
                                                                     int min_blocks,
                                                                     uint64_t* __restrict__ mask) {
   __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][2048];
+  __shared__ float zs[TW_WAVES];
+  __shared__ int ks[TW_WAVES];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const long long row = (long long)blockIdx.x * TW_WAVES + wv;
-  if (row >= n_rows) return;
-  const float* s = scores + row * (long long)nk;
+  const bool valid = row < n_rows;
+  const float* s = scores + (valid ? row : 0ll) * (long long)nk;
   float* b = buf[wv];
   uint32_t* bu = reinterpret_cast<uint32_t*>(b);
 
@@ -550,7 +561,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave2_kernel(const float* 
     if (1024 + 16 * lane + e < nk) bu[1024 + 16 * lane + e] = c[e];
   }
   wave_lds_sync();
-  const int kk = topp_count(b, nk, mx, p, min_blocks, lane);
+  const int kk = topp_count(buf, zs, ks, nk, mx, p, min_blocks, lane, wv);
   const int pos = kk - 1;
   uint32_t cand = 0u;
 #pragma unroll
@@ -564,7 +575,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave2_kernel(const float* 
   uint32_t o[16 + EW2];
 #pragma unroll
   for (int w = 0; w < 16 + EW2; ++w) o[w] = 64 * w + lane < nk ? ord_bits(s[64 * w + lane]) : 0u;
-  emit_mask<16 + EW2>(o, nk, W, kstar, kk - n_gt, mask + row * (long long)W, lane);
+  if (valid) emit_mask<16 + EW2>(o, nk, W, kstar, kk - n_gt, mask + row * (long long)W, lane);
 }
 }  // namespace
 }  // namespace bsa
