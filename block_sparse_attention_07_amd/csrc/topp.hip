@@ -493,12 +493,15 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
 // 15 - e), A keeps the larger key and B the smaller, then each part is finished
 // by its own half-cleaners.  Sorted position r is then element r % 16 of lane
 // (r % 1024) / 16 of A for r < 1024 and of B otherwise.
+// Six waves per SIMD (at most 80 registers, a few of them spilled) and a row
+// buffer of only nk's bound (20 KB per workgroup at up to 1280 blocks) measure
+// faster than five waves without spills: the sequential scans are latency.
 template <int EW2>
-__global__ __launch_bounds__(64 * TW_WAVES) void topp_wave2_kernel(const float* __restrict__ scores,
+__global__ __launch_bounds__(64 * TW_WAVES, 6) void topp_wave2_kernel(const float* __restrict__ scores,
                                                                     int n_rows, int nk, int W, float p,
                                                                     int min_blocks,
                                                                     uint64_t* __restrict__ mask) {
-  __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][2048];
+  __shared__ __attribute__((aligned(16))) float buf[TW_WAVES][EW2 == 4 ? 1280 : 1536];
   __shared__ float zs[TW_WAVES];
   __shared__ int ks[TW_WAVES];
   const int lane = threadIdx.x & 63;
@@ -539,18 +542,13 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave2_kernel(const float* 
 #pragma unroll
   for (int e = 0; e < 16; ++e) c[e] = 16 * lane + e < 64 * EW2 ? bu[16 * lane + e] : 0u;
   wave_lds_sync();
-  {
-    uint32_t ya[16], yc[16];
+  // a[e] and c[15 - e] face each other's partner-lane copies
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      ya[e] = xmirror32<32>(c[15 - e]);
-      yc[e] = xmirror32<32>(a[15 - e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      a[e] = a[e] > ya[e] ? a[e] : ya[e];
-      c[e] = c[e] > yc[e] ? yc[e] : c[e];
-    }
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t ya = xmirror32<32>(c[15 - e]);
+    const uint32_t yc = xmirror32<32>(a[e]);
+    a[e] = a[e] > ya ? a[e] : ya;
+    c[15 - e] = c[15 - e] > yc ? yc : c[15 - e];
   }
   merge_stage<16, 2048, 512, false>(a, lane);
   merge_stage<16, 2048, 512, false>(c, lane);
