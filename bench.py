@@ -1,7 +1,7 @@
 """Benchmark: block-sparse attention at the Wan2.1-14B 720p layer shape on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
-                    [--sweep] [--aux] [--b128] [--cold] [--ceiling]
+                    [--sweep] [--aux] [--topp] [--b128] [--cold] [--ceiling]
 
 Workload (synthetic, seeded): 40 heads, head_dim 128, bf16, latent grid
 21x45x80 = 75,600 tokens (1182 blocks of 64); 8 heads keep every block, the
@@ -24,6 +24,8 @@ Reported on one JSON line:
          shape: speedup against 1/density (the analogue of ScalingAttention Fig. 5).
 --aux    (extra, to stderr) the HBM-bound kernels of the path (mask producers,
          block scores, top-p, permutation, resize, fidelity) in GB/s vs 8 TB/s.
+--topp   (extra, to stderr) the dynamic top-p layer end to end on its workload:
+         Hilbert gather of Q, K, V, block scores, top-p mask, attention, scatter.
 --b128   (extra, to stderr) the same layer under the same mask recipe drawn over
          128x128-token blocks and passed as 32-bit row words (ScalingAttention's CRM format).
 --cold   (extra, to stderr) steps timed one by one after a 512 MiB device write that
@@ -158,6 +160,45 @@ def b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
                       "speedup_vs_full": round(ms_full / ms, 3)}), file=sys.stderr, flush=True)
 
 
+def topp_layer(bsa, torch, timed):
+    """The dynamic top-p layer end to end on its own workload (Q and K carry the
+    per-frame rank-8 component): Hilbert gather of Q, K, V, mean-pooled block
+    scores, top-p 0.9 with at least 8 blocks, planner + block-sparse attention,
+    scatter of O back to token order.  Per-stage and whole-chain times (stderr)."""
+    import workloads
+    dev = torch.device("cuda", 0)
+    w = workloads.WORKLOADS["topp_wan14b"]
+    q, k, v = workloads.qkv(w)
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = tb(q), tb(k), tb(v)
+    del q, k, v
+    perm = torch.from_numpy(bsa.hilbert3d_order(*w.grid)).to(dev)
+    qp, kp, vp, o, y = (torch.empty_like(qd) for _ in range(5))
+    H, N, nb = w.n_heads, w.seq_len, w.n_blocks
+    scores = torch.empty((H, nb, nb), dtype=torch.float32, device=dev)
+    mask = torch.empty((H, nb, bsa.mask_words(N)), dtype=torch.int64, device=dev)
+    stages = {
+        "hilbert_gather_qkv": lambda: [bsa.permute_tokens(a, perm, out=b) for a, b in ((qd, qp), (kd, kp), (vd, vp))],
+        "block_scores": lambda: bsa.block_scores_meanpool(qp, kp, w.scale, out=scores),
+        "topp_mask": lambda: bsa.mask_from_block_scores_topp(scores, 0.9, 8, out=mask),
+        "plan_and_attention": lambda: bsa.sparse_attn(qp, kp, vp, mask, w.scale, out=o),
+        "scatter_o": lambda: bsa.permute_tokens(o, perm, inverse=True, out=y),
+    }
+    for fn in stages.values():
+        fn()
+    torch.cuda.synchronize()
+    kept = int(np.unpackbits(mask.cpu().numpy().view(np.uint8)).sum())
+    rec = {"topp_layer": "Wan2.1-14B 720p, Hilbert order, top-p 0.9, min 8 blocks",
+           "density": round(kept / (H * nb * nb), 4), "kept_tiles": kept}
+    for name, fn in stages.items():
+        rec[name + "_ms"] = round(timed(fn, 5), 3)
+    total = timed(lambda: [fn() for fn in stages.values()], 5)
+    rec["total_ms"] = round(total, 3)
+    rec["attention_share"] = round(rec["plan_and_attention_ms"] / total, 3)
+    rec["layer_tflops_on_kept_tiles"] = round(kept * tile_flops(w.head_dim) / (total * 1e-3) / 1e12, 1)
+    print(json.dumps(rec), file=sys.stderr, flush=True)
+
+
 def aux_kernels(bsa, torch, timed):
     """Effective bandwidth of the HBM-bound kernels on the configs' shapes."""
     dev = torch.device("cuda", 0)
@@ -251,6 +292,7 @@ def main():
                     help="short run for counter collection: a few planned launches plus a 1 GiB copy")
     ap.add_argument("--sweep", action="store_true", help="also run the density sweep (stderr)")
     ap.add_argument("--aux", action="store_true", help="also time the HBM-bound kernels (stderr)")
+    ap.add_argument("--topp", action="store_true", help="also time the dynamic top-p layer end to end (stderr)")
     ap.add_argument("--b128", action="store_true",
                     help="also time the layer under a 128x128-block mask in 32-bit words (stderr)")
     ap.add_argument("--cold", action="store_true",
@@ -362,6 +404,8 @@ def main():
         density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
     if args.aux:
         aux_kernels(bsa, torch, timed)
+    if args.topp:
+        topp_layer(bsa, torch, timed)
     if args.b128:
         b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
     if args.cold:
