@@ -12,6 +12,9 @@ Because the kept set is an integer decision taken on floating-point sums, the
 selection is defined by one float32 procedure that the GPU kernel also follows,
 so both sides decide identically.  For one row of n scores s:
 
+0. s = min(max(s, -FLT_MAX), FLT_MAX), with a NaN score taking -FLT_MAX (the
+   pages only consider finite scores; this reading makes a row with NaN or
+   infinite scores a row of finite ones, so the steps below stay defined)
 1. m = max(s)
 2. e_j = EXP(s_j - m)               (float32 subtraction, then EXP below)
 3. order = indices by s descending, ties to the lower index
@@ -58,12 +61,21 @@ def exp32(x: np.ndarray) -> np.ndarray:
     return np.where(x < EXP_FLOOR, F(0.0), y).astype(F)
 
 
+FMAX = np.finfo(F).max
+
+
+def clamp_scores(s: np.ndarray) -> np.ndarray:
+    """Step 0: NaN -> -FLT_MAX, +-inf -> +-FLT_MAX (fmax / fmin drop a NaN operand)."""
+    return np.fmin(np.fmax(np.asarray(s, dtype=F), -FMAX), FMAX).astype(F)
+
+
 def select_row(s: np.ndarray, p: float, min_blocks: int) -> np.ndarray:
     """Kept key-block indices (in selection order) for one score row."""
-    s = np.asarray(s, dtype=F)
+    s = clamp_scores(s)
     n = s.size
     m = s.max()
-    e = exp32((s - m).astype(F))
+    with np.errstate(over="ignore"):
+        e = exp32((s - m).astype(F))          # -FLT_MAX - FLT_MAX overflows to -inf: EXP gives 0
     order = np.argsort(-s, kind="stable")
     e_sorted = e[order]
     z = np.cumsum(e_sorted, dtype=F)[-1]                  # sequential float32 sum

@@ -104,3 +104,50 @@ def test_selection_mass_reaches_p():
         # dropping the smallest kept block falls below p (unless min-k binds)
         if keep[0, u].sum() > 8:
             assert kept_mass - pr[keep[0, u]].min() < 0.9 + 1e-5
+
+
+def test_all_nan_row_reads_as_equal_scores():
+    """A row of NaN scores clamps to a row of equal scores: equal shares, so the
+    lowest-index prefix that reaches p (25 of 50 at p = 1/2), as for equal scores."""
+    s = np.full((1, 1, 50), np.nan, F)
+    keep = topp.topp_keep(s, 0.5, 0)[0, 0]
+    assert keep[:25].all() and not keep[25:].any()
+
+
+def test_positive_infinity_takes_all_mass():
+    """One +inf among finite scores: every other exponential underflows to 0 against
+    it, so k_p = 1 and the top-k minimum adds the 7 best finite blocks (score
+    descending, lower index first on ties)."""
+    s = workloads.random_scores(1, 1, 300, seed=8)
+    s[0, 0, 123] = np.inf
+    s[0, 0, 7] = s[0, 0, 9]                      # a tie among the finite scores
+    keep = topp.topp_keep(s, 0.9, 8)[0, 0]
+    others = np.array([j for j in np.argsort(-s[0, 0].astype(np.float64), kind="stable") if j != 123])
+    want = np.zeros(300, bool)
+    want[123] = True
+    want[others[:7]] = True
+    assert np.array_equal(keep, want)
+    assert topp.topp_keep(s, 0.9, 1)[0, 0].sum() == 1
+
+
+def test_nan_and_negative_infinity_rank_below_every_finite_score():
+    """NaN and -inf both read as -FLT_MAX: they are kept only once every finite block
+    is, and then in index order.  (An oracle without the clamp keeps the whole row,
+    since a NaN maximum makes every sum NaN.)"""
+    rng = np.random.default_rng(9)
+    s = (rng.standard_normal(30) * 3).astype(F)
+    idx = rng.permutation(30)
+    s[idx[:5]] = np.nan
+    s[idx[5:10]] = -np.inf
+    finite = np.sort(idx[10:])
+    low = np.sort(idx[:10])
+    keep = topp.topp_keep(s[None, None], 1e-6, 20)[0, 0]
+    assert np.array_equal(np.flatnonzero(keep), finite)
+    keep = topp.topp_keep(s[None, None], 1e-6, 22)[0, 0]
+    assert np.array_equal(np.flatnonzero(keep), np.sort(np.concatenate([finite, low[:2]])))
+    # the mass of p is carried by the finite blocks alone
+    fin = s[finite].astype(np.float64)
+    pr = np.exp(fin - fin.max())
+    pr /= pr.sum()
+    kept = topp.topp_keep(s[None, None], 0.9, 0)[0, 0]
+    assert not kept[low].any() and pr[np.isin(finite, np.flatnonzero(kept))].sum() >= 0.9 - 1e-6
