@@ -9,7 +9,10 @@
 // with -ffp-contract=off and the arithmetic sits under `fp contract(off)`), the
 // sums run sequentially in sorted order, and the exponential is the library's
 // own (Cody-Waite reduction with a two-part ln 2, degree-7 Taylor polynomial in
-// Horner form, 2^n assembled from exponent bits, 0 below -87).
+// Horner form, 2^n assembled from exponent bits, 0 below -87).  Scores are read
+// through one clamp, NaN to -FLT_MAX and +-inf to +-FLT_MAX, before anything
+// else (the pages only consider finite scores; this makes the result defined,
+// and the same for every row length, when some are not).
 //
 // Rows of up to 2048 blocks: one wave per row, the row held as 32-bit keys in
 // registers and sorted inside the wave by a bitonic network in mirror form (no
@@ -20,6 +23,7 @@
 // sorted mostly inside threads and waves, the chosen blocks OR-ed into LDS
 // words.  Either way the exponentials are summed and scanned by one lane in
 // sorted order.
+#include <cfloat>
 #include <cmath>
 
 #include "bsa_internal.h"
@@ -60,6 +64,11 @@ __device__ float exp_cw(float x) {
   const float two_n = __int_as_float((ni + 127) << 23);
   return p * two_n;
 }
+
+// Non-finite scores: NaN reads as the lowest finite score and +-inf as the
+// largest finite magnitudes (maxNum / minNum drop a NaN operand), so every
+// kernel width sees a total order and the same sums.
+__device__ __forceinline__ float clamp_score(float x) { return fminf(fmaxf(x, -FLT_MAX), FLT_MAX); }
 
 __device__ __forceinline__ bool before(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
@@ -177,7 +186,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(const float* __restrict__ scor
   for (int e = 0; e < E; ++e) {
     const int j = E * tid + e;
     if (j < nk) {
-      k[e] = s[j];
+      k[e] = clamp_score(s[j]);
       ix[e] = j;
       mx = fmaxf(mx, k[e]);
     } else {
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(64 * TW_WAVES) void topp_wave_kernel(const float* _
     const int j = 64 * e + lane;
     o[e] = 0u;
     if (j < nk) {
-      const float v = s[j];
+      const float v = clamp_score(s[j]);
       mx = fmaxf(mx, v);
       o[e] = ord_bits(v);
     }
@@ -516,7 +525,7 @@ __global__ __launch_bounds__(64 * TW_WAVES, 6) void topp_wave2_kernel(const floa
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const float v = s[64 * e + lane];                 // blocks 0 .. 1023 all exist
+    const float v = clamp_score(s[64 * e + lane]);    // blocks 0 .. 1023 all exist
     mx = fmaxf(mx, v);
     a[e] = ord_bits(v);
   }
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(64 * TW_WAVES, 6) void topp_wave2_kernel(const floa
     const int j = 1024 + 64 * e + lane;
     c2[e] = 0u;
     if (j < nk) {
-      const float v = s[j];
+      const float v = clamp_score(s[j]);
       mx = fmaxf(mx, v);
       c2[e] = ord_bits(v);
     }
@@ -572,7 +581,7 @@ __global__ __launch_bounds__(64 * TW_WAVES, 6) void topp_wave2_kernel(const floa
   // costs more registers than the two-part sort leaves)
   uint32_t o[16 + EW2];
 #pragma unroll
-  for (int w = 0; w < 16 + EW2; ++w) o[w] = 64 * w + lane < nk ? ord_bits(s[64 * w + lane]) : 0u;
+  for (int w = 0; w < 16 + EW2; ++w) o[w] = 64 * w + lane < nk ? ord_bits(clamp_score(s[64 * w + lane])) : 0u;
   if (valid) emit_mask<16 + EW2>(o, nk, W, kstar, kk - n_gt, mask + row * (long long)W, lane);
 }
 }  // namespace

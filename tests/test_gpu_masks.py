@@ -76,6 +76,32 @@ def test_topp_bit_exact_random_scores(nk):
         assert np.array_equal(gu.mask_host(m), topp.topp_mask_bits(s, p, mb)), (p, mb)
 
 
+@pytest.mark.parametrize("nk", [300, 1182, 1400, 2048, 3000])
+def test_topp_non_finite_scores_bit_exact(nk):
+    """NaN and +-inf scores take the clamp rule (NaN -> -FLT_MAX, +-inf -> +-FLT_MAX)
+    in every kernel width: the one-wave rows (300, 2048 blocks), the two-part rows
+    (1182, 1400) and the workgroup rows (3000), bit for bit with the oracle."""
+    s = workloads.random_scores(2, 9, nk, seed=nk + 1)
+    rng = np.random.default_rng(nk)
+    for r in range(9):
+        idx = rng.choice(nk, size=12, replace=False)
+        s[0, r, idx[:4]] = np.nan
+        s[0, r, idx[4:8]] = -np.inf
+        s[0, r, idx[8:10]] = np.float32(-np.nan)     # negative-signed NaN
+        if r % 3 == 0:
+            s[0, r, idx[10]] = np.inf
+        if r % 3 == 1:
+            s[0, r, idx[10:12]] = np.inf               # two tied infinities
+    s[1, 0] = np.nan                                    # a whole row of NaN
+    s[1, 1] = -np.inf
+    s[1, 2, :] = np.inf
+    sd = gu.to_dev(s)
+    for p, mb in [(0.9, 8), (1e-6, 8), (1.0, 0), (0.5, nk - 3)]:
+        m = bsa.mask_from_block_scores_topp(sd, p, mb)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.mask_host(m), topp.topp_mask_bits(s, p, mb)), (p, mb)
+
+
 def test_block_scores_within_fp32_bound():
     n, d = 64 * 37 + 9, 128
     rng = np.random.default_rng(22)
@@ -150,6 +176,9 @@ def test_topp_pipeline_end_to_end():
     out = bsa.permute_tokens(yd, pd, inverse=True)
     torch.cuda.synchronize()
     bits_gpu = gu.mask_host(mask)
+    # the selection itself is bit-exact: the oracle's float32 procedure on the GPU's
+    # own scores gives the GPU's mask on every one of the 47,280 rows
+    assert np.array_equal(bits_gpu, topp.topp_mask_bits(sc.cpu().numpy(), p, mb))
     # oracle pipeline: float64 scores, rounded once to float32, then the float32 selection
     qp = hilbert.permute_rows(q, perm)
     kp = hilbert.permute_rows(k, perm)
