@@ -30,5 +30,6 @@ from .api import (  # noqa: F401
     sparse_attn,
     sparse_attn_b128,
     threshold_map_resize,
+    workspace_bytes,
 )
 from ._lib import BsaError, LIB_PATH  # noqa: F401

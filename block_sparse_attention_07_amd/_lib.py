@@ -15,10 +15,12 @@ _p = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 
-# name -> argument types (every entry point returns int except bsa_last_error)
+# name -> argument types (every entry point returns int except those in RESTYPES)
 SIGNATURES = {
     "bsa_mask_words": [_i, _i],
     "sparse_attn_fwd": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],
+    "sparse_attn_workspace_bytes": [_i, _i, _i],
+    "sparse_attn_fwd_ws": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, ctypes.c_size_t, _p],
     "sparse_attn_fwd_f32": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],
     "sparse_attn_plan": [_p, _i, _i, _i, _p, _p, _p, _p],
     "sparse_attn_fwd_planned": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],
@@ -34,6 +36,7 @@ SIGNATURES = {
     "permute_tokens": [_p, _p, _i, _i, _i, _i, _i, _p, _p],
     "hilbert3d_order": [_i, _i, _i, _p],
 }
+RESTYPES = {"sparse_attn_workspace_bytes": ctypes.c_size_t}
 EXPORTS = ["bsa_last_error", *SIGNATURES]
 
 _lib = None
@@ -56,7 +59,7 @@ def lib() -> ctypes.CDLL:
         for name, args in SIGNATURES.items():
             fn = getattr(handle, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_int
+            fn.restype = RESTYPES.get(name, ctypes.c_int)
         _lib = handle
     return _lib
 

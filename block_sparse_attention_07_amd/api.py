@@ -69,10 +69,18 @@ def _check_mask(mask_bits, H, N):
           f"mask_bits must be [{H}, {nb}, {mask_words(N)}], got {tuple(mask_bits.shape)}")
 
 
+def workspace_bytes(n_heads: int, seq_len: int, head_dim: int) -> int:
+    """Device workspace bytes sparse_attn_fwd_ws needs (0 for invalid sizes)."""
+    return int(lib().sparse_attn_workspace_bytes(int(n_heads), int(seq_len), int(head_dim)))
+
+
 @_on_device
-def sparse_attn(q, k, v, mask_bits, scale=None, out=None, work_order=None):
+def sparse_attn(q, k, v, mask_bits, scale=None, out=None, work_order=None, workspace=None):
     """Block-sparse attention (sparse_attn_fwd / sparse_attn_fwd_f32 /
-    sparse_attn_fwd_planned).  q, k, v: [H, N, d] bf16 or fp32."""
+    sparse_attn_fwd_planned / sparse_attn_fwd_ws).  q, k, v: [H, N, d] bf16 or fp32.
+    ``workspace``: a caller-owned uint8 device tensor of at least
+    workspace_bytes(H, N, d) bytes (bf16, no work order) used instead of the
+    library's scratch buffer."""
     _dev(q, k, v, mask_bits)
     _need(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must share shape [H, N, d]")
     _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
@@ -84,7 +92,15 @@ def sparse_attn(q, k, v, mask_bits, scale=None, out=None, work_order=None):
     _dev(q, out)
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     s = _stream(q)
-    if q.dtype == torch.bfloat16:
+    _need(workspace is None or (q.dtype == torch.bfloat16 and work_order is None),
+          "a workspace is taken by the bf16 entry point without a work order")
+    if workspace is not None:
+        _dev(q, workspace)
+        _need(workspace.dtype == torch.uint8 and workspace.dim() == 1, "workspace must be a 1-D uint8 tensor")
+        rc = lib().sparse_attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits), H, N, d, BLOCK, BLOCK,
+                                      scale, _ptr(out), _ptr(workspace), workspace.numel(), s)
+        check(rc, "sparse_attn_fwd_ws")
+    elif q.dtype == torch.bfloat16:
         if work_order is None:
             rc = lib().sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits), H, N, d, BLOCK,
                                        BLOCK, scale, _ptr(out), s)

@@ -239,22 +239,25 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     k_rd[ks] = r * D * 2 + 16 * ((2 * ks + g) ^ k_swz<D>(r));
   }
 
-  // Buffer descriptors: one per head and tensor, a scalar byte offset for the
-  // tile and per-lane byte offsets fixed for the whole row.  The range check
-  // returns zeros for K rows past the sequence end (the ragged last block),
-  // which the softmax masks out; V^T rows are zero-padded there.
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)((uint32_t)N * D * 2u), BUFFER_DWORD3);
+  // Buffer descriptors with per-lane byte offsets fixed for the whole row.  A K
+  // descriptor starts at its tile and its num_records covers only the bytes from
+  // there to the end of the head's K, so the per-lane range check (on the lane
+  // offset alone; the scalar offset is 0) returns zeros for key rows past the
+  // sequence end (the ragged last block, masked out by the softmax) and no read
+  // leaves the tensor.  V^T rows are zero-padded to whole blocks, so every V^T
+  // tile lies inside its head's descriptor.
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(VTh), 0, (int)(D * npad * 2), BUFFER_DWORD3);
 
   auto kdma = [&](int kvb, int kbuf) {
 #ifdef __HIP_DEVICE_COMPILE__   // the host pass cannot form LDS address-space pointers
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(Kh + (size_t)kvb * BLK * D), 0, (N - kvb * BLK) * D * 2, BUFFER_DWORD3);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           krs, (__attribute__((address_space(3))) void*)(kstage(kbuf) + (wave_u * NI + i) * KR * D), 16,
-          k_voff[i], kvb * BLK * D * 2, 0, 0);
+          k_voff[i], 0, 0, 0);
 #endif
   };
   auto vdma = [&](int vvb, int vbuf) {
@@ -607,17 +610,18 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
   int k_rd[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) k_rd[ks] = r32 * D * 2 + 16 * ((2 * ks + g) ^ k_swz<D>(r32));
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(Kh), 0, (int)((uint32_t)N * D * 2u), BUFFER_DWORD3);
+  // K descriptors start at their tile (see attn_fwd_bf16_kernel).
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(VTh), 0, (int)(D * npad * 2), BUFFER_DWORD3);
   auto kdma = [&](int kvb, int kbuf) {
 #ifdef __HIP_DEVICE_COMPILE__
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(Kh + (size_t)kvb * BLK * D), 0, (N - kvb * BLK) * D * 2, BUFFER_DWORD3);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           krs, (__attribute__((address_space(3))) void*)(kstage(kbuf) + (wave_u * NI + i) * KR * D), 16,
-          k_voff[i], kvb * BLK * D * 2, 0, 0);
+          k_voff[i], 0, 0, 0);
 #endif
   };
   auto vdma = [&](int vvb, int vbuf) {
@@ -909,6 +913,37 @@ int launch_attn_bf16(const void* q, const void* k, const void* v, const uint64_t
 
 }  // namespace bsa
 
+namespace bsa {
+namespace {
+// Workspace of the unplanned bf16 entry points: row counts, head totals and the
+// work order of the planner, then the transposed V; every part 256-byte aligned.
+struct AttnWorkspace {
+  size_t off_tiles, off_order, off_vt, bytes;
+};
+AttnWorkspace attn_workspace(int n_heads, int seq_len, int head_dim) {
+  const size_t rows = (size_t)n_heads * n_blocks(seq_len, 64);
+  AttnWorkspace w;
+  w.off_tiles = (rows * 4 + 255) & ~size_t(255);
+  w.off_order = (w.off_tiles + (size_t)n_heads * 8 + 255) & ~size_t(255);
+  w.off_vt = (w.off_order + rows * 4 + 255) & ~size_t(255);
+  w.bytes = w.off_vt + vt_bytes(n_heads, seq_len, head_dim);
+  return w;
+}
+int attn_with_workspace(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                        int n_heads, int seq_len, int head_dim, float scale, void* out, char* ws,
+                        hipStream_t stream) {
+  const AttnWorkspace w = attn_workspace(n_heads, seq_len, head_dim);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws);
+  int64_t* tiles = reinterpret_cast<int64_t*>(ws + w.off_tiles);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + w.off_order);
+  int rc = launch_plan(mask_bits, n_heads, seq_len, counts, tiles, order, stream);
+  if (rc) return rc;
+  return launch_attn_bf16(q, k, v, mask_bits, order, n_heads, seq_len, head_dim, scale, out,
+                          ws + w.off_vt, stream);
+}
+}  // namespace
+}  // namespace bsa
+
 extern "C" int sparse_attn_fwd(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
                                int n_heads, int seq_len, int head_dim, int block_q, int block_k,
                                float scale, void* out, hipStream_t stream) {
@@ -916,19 +951,35 @@ extern "C" int sparse_attn_fwd(const void* q, const void* k, const void* v, cons
   int rc = check_attn_args(q, k, v, mask_bits, out, n_heads, seq_len, head_dim, block_q, block_k,
                            scale, 16);
   if (rc) return rc;
-  const size_t rows = (size_t)n_heads * n_blocks(seq_len, 64);
-  const size_t off_tiles = (rows * 4 + 255) & ~size_t(255);
-  const size_t off_order = (off_tiles + (size_t)n_heads * 8 + 255) & ~size_t(255);
-  const size_t off_vt = (off_order + rows * 4 + 255) & ~size_t(255);
-  char* ws = static_cast<char*>(scratch(off_vt + vt_bytes(n_heads, seq_len, head_dim), stream));
+  ScratchLease lease(attn_workspace(n_heads, seq_len, head_dim).bytes);
+  char* ws = static_cast<char*>(lease.get());
   if (!ws) return BSA_ERR_HIP;
-  int32_t* counts = reinterpret_cast<int32_t*>(ws);
-  int64_t* tiles = reinterpret_cast<int64_t*>(ws + off_tiles);
-  int32_t* order = reinterpret_cast<int32_t*>(ws + off_order);
-  rc = launch_plan(mask_bits, n_heads, seq_len, counts, tiles, order, stream);
+  return attn_with_workspace(q, k, v, mask_bits, n_heads, seq_len, head_dim, scale, out, ws, stream);
+}
+
+extern "C" size_t sparse_attn_workspace_bytes(int n_heads, int seq_len, int head_dim) {
+  using namespace bsa;
+  if (n_heads < 1 || seq_len < 1 || (head_dim != 64 && head_dim != 128)) return 0;
+  if ((long long)n_heads * n_blocks(seq_len, 64) > 0x7fffffffLL) return 0;
+  return attn_workspace(n_heads, seq_len, head_dim).bytes;
+}
+
+extern "C" int sparse_attn_fwd_ws(const void* q, const void* k, const void* v,
+                                  const uint64_t* mask_bits, int n_heads, int seq_len, int head_dim,
+                                  int block_q, int block_k, float scale, void* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  using namespace bsa;
+  int rc = check_attn_args(q, k, v, mask_bits, out, n_heads, seq_len, head_dim, block_q, block_k,
+                           scale, 16);
   if (rc) return rc;
-  return launch_attn_bf16(q, k, v, mask_bits, order, n_heads, seq_len, head_dim, scale, out,
-                          ws + off_vt, stream);
+  if (!workspace || !aligned(workspace, 256))
+    return fail(BSA_ERR_INVALID_ARG, "workspace must be a non-null 256-byte aligned device pointer");
+  const size_t need = attn_workspace(n_heads, seq_len, head_dim).bytes;
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_INVALID_ARG, "workspace holds %zu bytes, this call needs %zu", workspace_bytes,
+                need);
+  return attn_with_workspace(q, k, v, mask_bits, n_heads, seq_len, head_dim, scale, out,
+                             static_cast<char*>(workspace), stream);
 }
 
 extern "C" int sparse_attn_fwd_planned(const void* q, const void* k, const void* v,
@@ -941,7 +992,8 @@ extern "C" int sparse_attn_fwd_planned(const void* q, const void* k, const void*
   if (rc) return rc;
   if (!work_order || !aligned(work_order, 4))
     return fail(BSA_ERR_INVALID_ARG, "work_order must be a non-null 4-byte aligned pointer");
-  void* vt = scratch(vt_bytes(n_heads, seq_len, head_dim), stream);
+  ScratchLease lease(vt_bytes(n_heads, seq_len, head_dim));
+  void* vt = lease.get();
   if (!vt) return BSA_ERR_HIP;
   return launch_attn_bf16(q, k, v, mask_bits, work_order, n_heads, seq_len, head_dim, scale, out,
                           vt, stream);

@@ -96,7 +96,8 @@ extern "C" int sparse_attn_fwd_b128(const void* q, const void* k, const void* v,
   const size_t off_order = (off_tiles + (size_t)n_heads * 8 + 255) & ~size_t(255);
   const size_t off_mask = (off_order + rows * 4 + 255) & ~size_t(255);
   const size_t off_vt = (off_mask + rows * n_words(nb) * 8 + 255) & ~size_t(255);
-  char* ws = static_cast<char*>(scratch(off_vt + vt_bytes(n_heads, seq_len, head_dim), stream));
+  ScratchLease lease(off_vt + vt_bytes(n_heads, seq_len, head_dim));
+  char* ws = static_cast<char*>(lease.get());
   if (!ws) return BSA_ERR_HIP;
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   int64_t* tiles = reinterpret_cast<int64_t*>(ws + off_tiles);

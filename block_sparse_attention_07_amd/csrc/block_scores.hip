@@ -283,7 +283,8 @@ extern "C" int block_scores_meanpool(const void* q, const void* k, int n_heads, 
     return fail(BSA_ERR_INVALID_ARG, "problem too large");
   // pooled means as three bf16 parts: [Q, K][part][n_heads][nb][head_dim]
   const size_t split_bytes = (size_t)6 * n_heads * nb * head_dim * sizeof(unsigned short);
-  auto* split = static_cast<unsigned short*>(scratch(split_bytes, stream));
+  ScratchLease lease(split_bytes);
+  auto* split = static_cast<unsigned short*>(lease.get());
   if (!split) return BSA_ERR_HIP;
   const auto* qq = static_cast<const unsigned short*>(q);
   const auto* kk = static_cast<const unsigned short*>(k);

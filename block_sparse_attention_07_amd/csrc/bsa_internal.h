@@ -17,9 +17,23 @@ int ok();
 // Map a HIP status to BSA_ERR_HIP with the call site named.
 int hip_fail(hipError_t e, const char* what);
 
-// Per-device scratch buffer owned by the library, grown on demand.  Returns
-// nullptr (with the error recorded) when allocation fails.
-void* scratch(size_t bytes, hipStream_t stream);
+// Per-device scratch buffer owned by the library, grown on demand.  A lease
+// holds the current device's scratch lock from construction to destruction, so
+// an entry point keeps its lease until every launch that uses the buffer is
+// enqueued; another thread can then never free the buffer under it.  get() is
+// nullptr (with the error recorded) when the buffer could not be provided.
+class ScratchLease {
+ public:
+  explicit ScratchLease(size_t bytes);
+  ~ScratchLease();
+  ScratchLease(const ScratchLease&) = delete;
+  ScratchLease& operator=(const ScratchLease&) = delete;
+  void* get() const { return ptr_; }
+
+ private:
+  int dev_ = -1;
+  void* ptr_ = nullptr;
+};
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

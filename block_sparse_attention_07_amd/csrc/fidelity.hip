@@ -212,7 +212,8 @@ extern "C" int attn_fidelity(const void* q, const void* k, const uint64_t* mask_
   const int nb = n_blocks(seq_len, 64);
   const int W = n_words(nb);
   const int n_chunks = (seq_len + CHUNK - 1) / CHUNK;
-  float* part = static_cast<float*>(scratch((size_t)n_heads * n_rows * n_chunks * 3 * sizeof(float), stream));
+  ScratchLease lease((size_t)n_heads * n_rows * n_chunks * 3 * sizeof(float));
+  float* part = static_cast<float*>(lease.get());
   if (!part) return BSA_ERR_HIP;
   const float c = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)n_chunks, (unsigned)n_heads, (unsigned)((n_rows + RG - 1) / RG));

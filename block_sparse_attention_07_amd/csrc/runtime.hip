@@ -14,10 +14,10 @@ thread_local char g_msg[512] = "";
 
 constexpr int kMaxDevices = 64;
 struct Scratch {
+  std::mutex mu;          // held by a lease from acquisition until its entry point returns
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-std::mutex g_scratch_mu;
 Scratch g_scratch[kMaxDevices];
 }  // namespace
 
@@ -38,27 +38,34 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(BSA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
 }
 
-void* scratch(size_t bytes, hipStream_t stream) {
+// The device's buffer is only ever replaced by a thread that holds its lock, and
+// every entry point that uses the buffer holds the lock until all of its launches
+// are enqueued.  So when a larger buffer is needed, every launch that can touch
+// the old one is already on some stream, and one device-wide synchronisation
+// covers them all before the old buffer is freed.
+ScratchLease::ScratchLease(size_t bytes) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
     hip_fail(e, "hipGetDevice");
-    return nullptr;
+    return;
   }
   if (dev < 0 || dev >= kMaxDevices) {
     fail(BSA_ERR_UNSUPPORTED, "device ordinal %d exceeds %d", dev, kMaxDevices);
-    return nullptr;
+    return;
   }
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
   Scratch& s = g_scratch[dev];
-  if (s.bytes >= bytes && s.ptr) return s.ptr;
-  // Work already enqueued may still read the old buffer: wait for the whole
-  // device before releasing it.
+  s.mu.lock();
+  dev_ = dev;
+  if (s.bytes >= bytes && s.ptr) {
+    ptr_ = s.ptr;
+    return;
+  }
   if (s.ptr) {
     e = hipDeviceSynchronize();
     if (e != hipSuccess) {
       hip_fail(e, "hipDeviceSynchronize (scratch growth)");
-      return nullptr;
+      return;
     }
     (void)hipFree(s.ptr);
     s.ptr = nullptr;
@@ -70,12 +77,15 @@ void* scratch(size_t bytes, hipStream_t stream) {
   e = hipMalloc(&p, want);
   if (e != hipSuccess) {
     hip_fail(e, "hipMalloc (scratch)");
-    return nullptr;
+    return;
   }
-  (void)stream;
   s.ptr = p;
   s.bytes = want;
-  return p;
+  ptr_ = p;
+}
+
+ScratchLease::~ScratchLease() {
+  if (dev_ >= 0) g_scratch[dev_].mu.unlock();
 }
 
 int check_attn_args(const void* q, const void* k, const void* v, const void* mask, const void* out,

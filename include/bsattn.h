@@ -41,6 +41,7 @@
 #ifndef BSATTN_H
 #define BSATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -79,12 +80,41 @@ int bsa_mask_words(int seq_len, int block);
  * in decreasing kept-block count).  V is first copied transposed ([n_heads][head_dim]
  * [nb * 64], zero-padded) so its tiles stream like K's.  The plan and the transposed
  * V live in a library-owned per-device scratch buffer that grows on demand (the
- * first call at a larger size synchronises the device to grow it); calls that
- * overlap on one device from different streams race on that buffer.
+ * first call at a larger size synchronises the device, then frees the old buffer,
+ * so it must not run under stream capture).  Host threads may call concurrently:
+ * each call holds the device's scratch lock until its launches are enqueued, so a
+ * buffer is never freed under a call.  But the buffer's contents are shared:
+ * calls whose kernels overlap on one device (different streams) race on them.
+ * sparse_attn_fwd_ws below takes a caller workspace instead.
  */
 int sparse_attn_fwd(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
                     int n_heads, int seq_len, int head_dim, int block_q, int block_k,
                     float scale, void* out, hipStream_t stream);
+
+/*
+ * sparse_attn_workspace_bytes -- bytes of device workspace sparse_attn_fwd_ws needs
+ * for this shape: the plan (int32 row counts and work order [n_heads * nb], int64
+ * head totals [n_heads]) and the transposed V (bf16 [n_heads][head_dim][nb * 64]),
+ * each part 256-byte aligned.  0 when the arguments are invalid (n_heads or
+ * seq_len < 1, head_dim not 64 or 128, n_heads * nb >= 2^31).
+ */
+size_t sparse_attn_workspace_bytes(int n_heads, int seq_len, int head_dim);
+
+/*
+ * sparse_attn_fwd_ws -- sparse_attn_fwd with a caller-owned workspace in place of
+ * the library's scratch buffer; it allocates, frees and synchronises nothing.
+ *   workspace        device pointer, 256-byte aligned, at least
+ *                    sparse_attn_workspace_bytes(n_heads, seq_len, head_dim) bytes;
+ *                    its contents on entry do not matter and are not preserved.
+ *   workspace_bytes  its size; a smaller size is BSA_ERR_INVALID_ARG.
+ * Calls with distinct workspaces are independent of each other on any streams and
+ * threads; two calls sharing a workspace must be ordered by the caller.  Other
+ * arguments and behaviour as sparse_attn_fwd (bf16 only).
+ */
+int sparse_attn_fwd_ws(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                       int n_heads, int seq_len, int head_dim, int block_q, int block_k,
+                       float scale, void* out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /*
  * sparse_attn_fwd_f32 -- same operation and arguments with fp32 q, k, v, out and
@@ -217,7 +247,10 @@ int block_scores_meanpool(const void* q, const void* k, int n_heads, int seq_len
  *   c >= p gives k_p (k_p = n if never);  keep the first max(k_p, min(min_blocks, n))
  *   blocks of the order.
  *
- *   scores      fp32 [n_heads][n_q_blocks][n_k_blocks], finite; 1 <= n_k_blocks <= 4096.
+ *   scores      fp32 [n_heads][n_q_blocks][n_k_blocks]; 1 <= n_k_blocks <= 4096.  Each
+ *               score is first clamped: NaN becomes -FLT_MAX, +inf FLT_MAX and -inf
+ *               -FLT_MAX (so a NaN block is kept only when the top-k minimum or p
+ *               reaches the lowest scores, lower-index ties first).
  *   p           in (0, 1];  min_blocks >= 0.
  *   mask_bits   uint64 [n_heads][n_q_blocks][ceil(n_k_blocks/64)], written in full.
  */
@@ -303,10 +336,13 @@ int permute_tokens(const void* x, const int32_t* perm, int n_heads, int seq_len,
                    int elem_bytes, int inverse, void* y, hipStream_t stream);
 
 /*
- * hilbert3d_order -- host-only, synchronous.  perm_host (int32 [T*H*W], host memory)
- * receives the token ids (t-major id t*H*W + y*W + x) in increasing 3D Hilbert index,
- * using J. Skilling's transpose construction ("Programming the Hilbert curve", 2004)
- * on the smallest 2^b cube holding the grid, axes ordered (t, y, x).
+ * hilbert3d_order -- host-only, synchronous.  The token reordering that DFSAttn
+ * applies before block-sparse attention (DFSAttn abstract: tokens reordered along a
+ * Hilbert curve so that tokens close in space and time share blocks).  The page names
+ * the curve only; perm_host (int32 [T*H*W], host memory) receives the token ids
+ * (t-major id t*H*W + y*W + x) in increasing 3D Hilbert index, using J. Skilling's
+ * transpose construction ("Programming the Hilbert curve", 2004) on the smallest 2^b
+ * cube holding the grid, axes ordered (t, y, x).
  * T, H, W >= 1 and T*H*W < 2^31.
  */
 int hilbert3d_order(int T, int H, int W, int32_t* perm_host);

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(names) == sorted(_lib.EXPORTS)
 
 
@@ -30,6 +30,31 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
+
+
+def test_workspace_bytes_layout():
+    """Plan (row counts, head totals, work order) then the transposed V, each part
+    256-byte aligned; invalid sizes give 0."""
+    L = _lib.lib()
+    up = lambda x: -(-x // 256) * 256
+    for H, N, d in [(1, 1, 64), (2, 200, 128), (40, 75600, 128), (24, 126720, 128), (7, 4097, 64)]:
+        nb = -(-N // 64)
+        rows = H * nb
+        off_vt = up(up(up(rows * 4) + H * 8) + rows * 4)
+        assert L.sparse_attn_workspace_bytes(H, N, d) == off_vt + H * d * nb * 64 * 2
+    for H, N, d in [(0, 64, 128), (1, 0, 128), (1, 64, 96)]:
+        assert L.sparse_attn_workspace_bytes(H, N, d) == 0
+
+
+@pytest.mark.parametrize("ws,nbytes", [(None, 1 << 30), (8 * 16, 1 << 30), (256, 100)])
+def test_workspace_argument_errors_precede_any_device_call(ws, nbytes):
+    """A missing or misaligned workspace, or one smaller than the shape needs, is an
+    argument error returned before any HIP call."""
+    L = _lib.lib()
+    a = list(_attn_args())
+    w = ctypes.c_void_p(ws) if ws else None
+    assert L.sparse_attn_fwd_ws(*a[:11], w, nbytes, None) == 1
+    assert L.bsa_last_error().decode()
 
 
 def test_mask_words():

@@ -375,3 +375,71 @@ def test_pairs_of_identical_rows(n, d):
     got2 = _run_bf16(q, k, v, bits, 1 / np.sqrt(d), work_order=perm)
     for h in range(H):
         gu.assert_bf16_close(got2[h], ref[h], f"head {h} permuted")
+
+
+def test_caller_workspace_matches_library_scratch():
+    """sparse_attn_fwd_ws with a caller workspace gives the same bits as
+    sparse_attn_fwd (same plan, same kernels), on two shapes in a row with one
+    workspace sized for the larger, and matches the oracle."""
+    cases = [(3, 64 * 21 + 9, 128), (2, 64 * 6 + 1, 64)]
+    need = max(bsa.workspace_bytes(H, n, d) for H, n, d in cases)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for H, n, d in cases:
+        q, k, v = _rand_bf16(H, n, d, seed=31 + n)
+        nb = -(-n // B)
+        keep = np.random.default_rng(n).random((H, nb, nb)) < 0.35
+        keep[0, 1] = False
+        bits = crm.pack_rows(keep)
+        scale = 1.0 / np.sqrt(d)
+        a = _run_bf16(q, k, v, bits, scale)
+        b = _run_bf16(q, k, v, bits, scale, workspace=ws)
+        assert np.array_equal(a, b)
+        gu.assert_bf16_close(b, sparse_attention(_f(q), _f(k), _f(v), bits, scale), f"ws H={H} n={n} d={d}")
+    with pytest.raises(bsa.BsaError):
+        bsa.sparse_attn(gu.to_dev(q, True), gu.to_dev(k, True), gu.to_dev(v, True), gu.to_dev(bits), scale,
+                        workspace=ws[:16])
+
+
+def test_host_threads_growing_the_scratch_buffer():
+    """Several host threads call the attention on the default stream at sizes larger
+    than any earlier test's, so the library's scratch buffer is replaced (device
+    synchronised, old buffer freed) while other threads are enqueueing work on it;
+    every result equals the one computed through a caller workspace, which leaves
+    the scratch buffer alone."""
+    import threading
+    H, d = 64, 128
+    sizes = [50000, 54000, 58000, 62000]            # transposed V 0.82 .. 1.02 GB, above every other test
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    cases, want = [], []
+    ws = torch.empty(bsa.workspace_bytes(H, max(sizes), d), dtype=torch.uint8, device="cuda")
+    for n in sizes:
+        q, k, v = (torch.randn((H, n, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+        nb = -(-n // B)
+        keep = torch.rand((H, nb, nb), generator=g, device="cuda") < 0.02
+        W = -(-nb // 64)
+        pad = torch.zeros((H, nb, W * 64), dtype=torch.int64, device="cuda")
+        pad[..., :nb] = keep.to(torch.int64)
+        words = (pad.view(H, nb, W, 64) << torch.arange(64, device="cuda", dtype=torch.int64)).sum(-1)
+        cases.append((q, k, v, words))
+        want.append(bsa.sparse_attn(q, k, v, words, 1 / np.sqrt(d), workspace=ws))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            torch.cuda.set_device(0)
+            for j in range(len(cases)):
+                out = bsa.sparse_attn(*cases[j], 1 / np.sqrt(d))
+                torch.cuda.synchronize()
+                if not torch.equal(out, want[j]):
+                    errors.append((t, j))
+        except Exception as e:          # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
