@@ -46,14 +46,22 @@ def test_brute_force_small():
 
 
 def test_hilbert_full_cube_is_a_unit_step_bijection():
-    for bits in (1, 2, 3):
+    """Every cube up to 2^7 (the cube that holds the 21 x 45 x 80 latent grid):
+    the index is a bijection onto [0, 8^b), consecutive indices are unit steps
+    on one axis, and each run of 8^(b-1) consecutive indices fills one octant
+    (the recursive structure of a Hilbert curve)."""
+    for bits in range(1, 8):
         side = 1 << bits
         g = np.stack(np.meshgrid(*[np.arange(side)] * 3, indexing="ij"), -1).reshape(-1, 3)
         idx = hilbert.hilbert_index(g, bits)
-        assert sorted(idx.tolist()) == list(range(side ** 3))
+        assert np.array_equal(np.sort(idx), np.arange(side ** 3))
         path = g[np.argsort(idx)]
         steps = np.abs(np.diff(path, axis=0)).sum(axis=1)
         assert np.all(steps == 1)
+        octant = (path >> (bits - 1)).reshape(8, -1, 3)
+        assert np.all(octant == octant[:, :1])
+        assert len({tuple(o) for o in octant[:, 0]}) == 8
+    assert hilbert.grid_bits(21, 45, 80) == 7
 
 
 def test_hilbert_2d_unit_steps():
