@@ -1,12 +1,12 @@
-"""Benchmark: block-sparse attention at the Wan2.1-14B 720p layer shape on one GPU.
+"""Benchmark: block-sparse attention on one GPU at the shapes of the video-DiT layers.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--profile]
-                    [--sweep] [--aux] [--topp] [--b128] [--cold] [--ceiling]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+                    [--profile] [--aux] [--b128] [--cold] [--ceiling]
 
-Workload (synthetic, seeded): 40 heads, head_dim 128, bf16, latent grid
-21x45x80 = 75,600 tokens (1182 blocks of 64); 8 heads keep every block, the
-other 32 keep a band |u-v| <= 1 plus uniformly random blocks up to a per-head
-density drawn from U[0.05, 0.40].
+Headline workload (synthetic, seeded): the Wan2.1-14B 720p layer, 40 heads,
+head_dim 128, bf16, latent grid 21x45x80 = 75,600 tokens (1182 blocks of 64);
+8 heads keep every block, the other 32 keep a band |u-v| <= 1 plus uniformly
+random blocks up to a per-head density drawn from U[0.05, 0.40].
 
 One step = one pass of the hot path on that layer: the tile scheduler (row
 popcounts, head order) and the block-sparse attention kernel, via
@@ -14,18 +14,25 @@ sparse_attn_fwd.  Inputs are resident in HBM before timing starts.
 
 Reported on one JSON line:
   value      effective TFLOP/s on kept blocks = kept tiles * 4*64*64*128 / step time
+             (mean over the K timed steps); median_ms_per_step from per-step events
   speedup_vs_full_mask   step time with an all-ones mask / step time with the workload mask
   roofline   one planned call of the attention path (V transpose, pair launch,
              single-row slices; events on its stream): algorithmic flops per call /
              average call time vs the bf16 MFMA peak
   cpu_baseline  the float64 CPU oracle on a bounded sample of query blocks
+  wan13b_480p, hunyuan_768   the other layer shapes, each with its step time,
+             effective TFLOP/s, speedup over the all-ones mask and roofline fraction
+             (HunyuanVideo: stripe masks expanded on the device by mask_from_stripes;
+             the expansion is timed on its own and is not inside the attention step)
+  topp_wan14b   the dynamic top-p layer end to end (Hilbert gather of Q, K, V, block
+             scores, top-p mask, planner + attention, scatter of O) with per-stage times
+  density_sweep  uniform random masks at 5 .. 100 % density on the headline shape:
+             speedup against 1/density (the analogue of ScalingAttention Fig. 5)
+  gpu_clock  SCLK / MCLK read by amd-smi while the headline step runs
+  --quick skips the extra layers, the top-p layer and the sweep.
 
---sweep  (extra, to stderr) uniform random masks at 5 .. 100 % density on the same
-         shape: speedup against 1/density (the analogue of ScalingAttention Fig. 5).
 --aux    (extra, to stderr) the HBM-bound kernels of the path (mask producers,
          block scores, top-p, permutation, resize, fidelity) in GB/s vs 8 TB/s.
---topp   (extra, to stderr) the dynamic top-p layer end to end on its workload:
-         Hilbert gather of Q, K, V, block scores, top-p mask, attention, scatter.
 --b128   (extra, to stderr) the same layer under the same mask recipe drawn over
          128x128-token blocks and passed as 32-bit row words (ScalingAttention's CRM format).
 --cold   (extra, to stderr) steps timed one by one after a 512 MiB device write that
@@ -40,6 +47,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -76,23 +84,40 @@ def read_traffic():
         return None
 
 
+def host_cpu():
+    """Threads this process may run on, and the CPU model (lscpu)."""
+    cores = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return cores, model
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return None
+
+
 def cpu_baseline(w, q, k, v, bits, keep, budget_s=12.0):
     """Time the float64 oracle on a seeded sample of query blocks until about
     budget_s seconds of CPU work; report kept-tile flops per second."""
     from oracle.attention import sparse_attention
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    cores, model = host_cpu()
     rng = np.random.default_rng(1234)
     nb = w.n_blocks
     order = rng.permutation(w.n_heads * nb)
     cache = {}
     tiles = 0
     blocks = 0
-    t0 = time.perf_counter()
     spent = 0.0
     for rid in order:
         h, u = divmod(int(rid), nb)
@@ -107,11 +132,73 @@ def cpu_baseline(w, q, k, v, bits, keep, budget_s=12.0):
         if spent >= budget_s and blocks >= 8:
             break
     value = tiles * tile_flops(w.head_dim) / spent / 1e12
+    threads = blas_threads()
     return {
-        "value": round(value, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "value": round(value, 6), "unit": "TFLOP/s", "cores": min(cores, threads) if threads else cores,
+        "kind": "oracle",
         "sample": f"{blocks} random (head, query block) rows of the same layer, {tiles} kept tiles, "
                   f"{spent:.1f} s of float64 numpy/BLAS",
+        "affinity_cores": cores, "blas_threads": threads, "cpu_model": model,
     }
+
+
+class Timer:
+    """HIP events on one stream: mean over a run of back-to-back steps, and the
+    median of the per-step intervals between consecutive events."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, fn, n):
+        torch = self.torch
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(self.stream)
+        for i in range(n):
+            fn()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+        return ev[0].elapsed_time(ev[n]) / n, per[n // 2]
+
+    def __call__(self, fn, n):
+        return self.run(fn, n)[0]
+
+
+def gpu_clock_while(fn, seconds=2.0):
+    """SCLK and MCLK as amd-smi reports them while fn runs back to back (None when
+    the tool is missing or its output is not understood)."""
+    import torch
+    try:
+        proc = subprocess.Popen(["amd-smi", "metric", "-g", "0", "--clock", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except Exception:
+        return None
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < seconds + 20:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+    try:
+        out, _ = proc.communicate(timeout=5)
+        return parse_amdsmi_clock(json.loads(out))
+    except Exception:
+        proc.kill()
+        proc.wait()
+        return None
+
+
+def parse_amdsmi_clock(js):
+    """Current GFX clock of each XCD (SCLK) and the memory clock (MCLK), in MHz, from
+    amd-smi's metric JSON (gpu_data[0].clock.gfx_N.clk and mem_0.clk)."""
+    clocks = js["gpu_data"][0]["clock"] if isinstance(js, dict) else js[0]["clock"]
+    cur = lambda dom: clocks[dom]["clk"]["value"] if isinstance(clocks[dom].get("clk"), dict) else None
+    gfx = [cur(k) for k in sorted(clocks) if k.startswith("gfx_") and cur(k) is not None]
+    mem = cur("mem_0") if "mem_0" in clocks else None
+    if not gfx:
+        return None
+    return {"sclk_mhz_per_xcd": gfx, "sclk_mhz_mean": round(sum(gfx) / len(gfx), 1), "mclk_mhz": mem,
+            "source": "amd-smi metric --clock, sampled once while the headline step runs back to back"}
 
 
 def device_uniform_mask(torch, H, nb, density, seed, dev):
@@ -127,44 +214,111 @@ def device_uniform_mask(torch, H, nb, density, seed, dev):
     return words, int(keep.sum().item())
 
 
-def density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
-    dev = qd.device
+def full_mask(torch, H, nb, dev):
+    W = -(-nb // 64)
+    words = np.zeros((nb, W), np.uint64)
+    words[:, :] = np.uint64(2 ** 64 - 1)
+    if nb % 64:
+        words[:, -1] = np.uint64((1 << (nb % 64)) - 1)
+    return torch.from_numpy(np.ascontiguousarray(np.broadcast_to(words, (H, nb, W))).view(np.int64)).to(dev)
+
+
+def density_sweep(bsa, torch, w, qd, kd, vd, out, timer, ms_full):
+    res = []
     for dens in (0.05, 0.10, 0.20, 0.40, 0.60, 0.80, 1.00):
-        md, kept = device_uniform_mask(torch, w.n_heads, w.n_blocks, dens, 100 + int(dens * 100), dev)
+        md, kept = device_uniform_mask(torch, w.n_heads, w.n_blocks, dens, 100 + int(dens * 100), qd.device)
         f = lambda: bsa.sparse_attn(qd, kd, vd, md, w.scale, out=out)
         f()
-        ms = timed(f, 5)
-        rec = {"sweep_density": dens, "kept_tiles": kept, "ms": round(ms, 3),
+        ms = timer(f, 5)
+        rec = {"density": dens, "kept_tiles": kept, "ms": round(ms, 3),
                "tflops": round(kept * tile_flops(w.head_dim) / (ms * 1e-3) / 1e12, 1),
                "speedup_vs_full": round(ms_full / ms, 3), "ideal_speedup": round(1 / dens, 3)}
-        print(json.dumps(rec), file=sys.stderr, flush=True)
+        print("[bench] sweep " + json.dumps(rec), file=sys.stderr, flush=True)
+        res.append(rec)
         del md
+    return res
 
 
-def b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
-    """The same layer with the mask recipe drawn over ScalingAttention's 128-token blocks,
-    passed as 32-bit row words.  Flops count the kept 64-token tiles of the same
-    mask (the expanded form), as the headline metric does."""
+def layer_record(w, kept, ms, ms_med, ms_full):
+    full = w.n_heads * w.n_blocks ** 2
+    tf = kept * tile_flops(w.head_dim) / (ms * 1e-3) / 1e12
+    return {
+        "n_heads": w.n_heads, "seq_len": w.seq_len, "head_dim": w.head_dim, "kept_tiles": kept,
+        "density": round(kept / full, 4), "ms": round(ms, 4), "median_ms": round(ms_med, 4),
+        "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "full_mask_ms": round(ms_full, 4),
+        "full_mask_tflops": round(full * tile_flops(w.head_dim) / (ms_full * 1e-3) / 1e12, 1),
+        "speedup_vs_full_mask": round(ms_full / ms, 3), "ideal_speedup": round(full / kept, 3),
+    }
+
+
+def static_layer(bsa, torch, name, timer, steps):
+    """A layer with a host-built static mask (Wan2.1-1.3B 480p recipe)."""
     import workloads
-    keep = workloads.mask_wan14b(w, block=128)
-    words = workloads.pack_bits32(keep)
-    wd = torch.from_numpy(words.view(np.int32)).to(qd.device)
-    m64 = bsa.mask_b128_to_b64(wd, w.seq_len)
-    kept = int(sum(int(x).bit_count() for x in m64.cpu().numpy().view(np.uint64).ravel()))
-    f = lambda: bsa.sparse_attn_b128(qd, kd, vd, wd, w.scale, out=out)
-    f()
-    ms = timed(f, 10)
-    print(json.dumps({"b128_layer": "Wan2.1-14B 720p, 128x128 blocks, 32-bit words",
-                      "density": round(float(keep.mean()), 4), "kept_64_tiles": kept, "ms": round(ms, 3),
-                      "tflops": round(kept * tile_flops(w.head_dim) / (ms * 1e-3) / 1e12, 1),
-                      "speedup_vs_full": round(ms_full / ms, 3)}), file=sys.stderr, flush=True)
+    dev = torch.device("cuda", 0)
+    w = workloads.WORKLOADS[name]
+    keep = workloads.masks(w)
+    bits = workloads.pack_bits(keep)
+    q, k, v = workloads.qkv(w)
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = tb(q), tb(k), tb(v)
+    del q, k, v
+    md = torch.from_numpy(bits.view(np.int64)).to(dev)
+    fd = full_mask(torch, w.n_heads, w.n_blocks, dev)
+    out = torch.empty_like(qd)
+    f = lambda: bsa.sparse_attn(qd, kd, vd, md, w.scale, out=out)
+    ff = lambda: bsa.sparse_attn(qd, kd, vd, fd, w.scale, out=out)
+    for _ in range(3):
+        f()
+    ms, med = timer.run(f, steps)
+    ff()
+    ms_full = timer(ff, max(3, steps // 3))
+    rec = layer_record(w, int(keep.sum()), ms, med, ms_full)
+    rec["workload"] = ("Wan2.1-1.3B 480p attention layer: 12 heads, head_dim 128, 21x30x52=32760 tokens, "
+                       "band + temporal stripes + random fill, density U[0.10,0.50] per head")
+    print(f"[bench] {name} " + json.dumps(rec), file=sys.stderr, flush=True)
+    return rec
 
 
-def topp_layer(bsa, torch, timed):
+def hunyuan_layer(bsa, torch, timer, steps):
+    """HunyuanVideo 768x1280 layer under PSA stripe masks expanded on the device."""
+    import workloads
+    dev = torch.device("cuda", 0)
+    w = workloads.WORKLOADS["hunyuan_768"]
+    params = torch.from_numpy(workloads.stripe_params(w)).to(dev)
+    T, F = w.grid[0], w.frame_tokens
+    md = bsa.mask_from_stripes(params, T, F, w.seq_len)
+    build = lambda: bsa.mask_from_stripes(params, T, F, w.seq_len, out=md)
+    build()
+    ms_build = timer(build, 10)
+    kept = int(np.unpackbits(md.cpu().numpy().view(np.uint8)).sum())
+    q, k, v = workloads.qkv(w)
+    tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    qd, kd, vd = tb(q), tb(k), tb(v)
+    del q, k, v
+    fd = full_mask(torch, w.n_heads, w.n_blocks, dev)
+    out = torch.empty_like(qd)
+    f = lambda: bsa.sparse_attn(qd, kd, vd, md, w.scale, out=out)
+    ff = lambda: bsa.sparse_attn(qd, kd, vd, fd, w.scale, out=out)
+    for _ in range(3):
+        f()
+    ms, med = timer.run(f, steps)
+    ff()
+    ms_full = timer(ff, 3)
+    rec = layer_record(w, kept, ms, med, ms_full)
+    rec["workload"] = ("HunyuanVideo 768x1280 attention layer: 24 heads, head_dim 128, 33x48x80=126720 tokens, "
+                       "PSA stripe tuples (5 heads full window)")
+    rec["mask_from_stripes_ms"] = round(ms_build, 4)
+    rec["mask_build_in_step"] = False
+    print("[bench] hunyuan_768 " + json.dumps(rec), file=sys.stderr, flush=True)
+    return rec
+
+
+def topp_layer(bsa, torch, timer):
     """The dynamic top-p layer end to end on its own workload (Q and K carry the
     per-frame rank-8 component): Hilbert gather of Q, K, V, mean-pooled block
     scores, top-p 0.9 with at least 8 blocks, planner + block-sparse attention,
-    scatter of O back to token order.  Per-stage and whole-chain times (stderr)."""
+    scatter of O back to token order.  Per-stage and whole-chain times."""
     import workloads
     dev = torch.device("cuda", 0)
     w = workloads.WORKLOADS["topp_wan14b"]
@@ -188,15 +342,37 @@ def topp_layer(bsa, torch, timed):
         fn()
     torch.cuda.synchronize()
     kept = int(np.unpackbits(mask.cpu().numpy().view(np.uint8)).sum())
-    rec = {"topp_layer": "Wan2.1-14B 720p, Hilbert order, top-p 0.9, min 8 blocks",
+    rec = {"workload": "Wan2.1-14B 720p, Q/K with a per-frame rank-8 component, Hilbert order, top-p 0.9, min 8 blocks",
            "density": round(kept / (H * nb * nb), 4), "kept_tiles": kept}
     for name, fn in stages.items():
-        rec[name + "_ms"] = round(timed(fn, 5), 3)
-    total = timed(lambda: [fn() for fn in stages.values()], 5)
+        rec[name + "_ms"] = round(timer(fn, 5), 3)
+    total = timer(lambda: [fn() for fn in stages.values()], 5)
     rec["total_ms"] = round(total, 3)
     rec["attention_share"] = round(rec["plan_and_attention_ms"] / total, 3)
     rec["layer_tflops_on_kept_tiles"] = round(kept * tile_flops(w.head_dim) / (total * 1e-3) / 1e12, 1)
-    print(json.dumps(rec), file=sys.stderr, flush=True)
+    rec["frac_of_peak"] = round(rec["layer_tflops_on_kept_tiles"] / PEAK_BF16_TFLOPS, 4)
+    rec["block_scores_GBps"] = round((2 * H * N * w.head_dim * 2 + H * nb * nb * 4) / (rec["block_scores_ms"] * 1e-3) / 1e9, 1)
+    print("[bench] topp_wan14b " + json.dumps(rec), file=sys.stderr, flush=True)
+    return rec
+
+
+def b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full):
+    """The same layer with the mask recipe drawn over ScalingAttention's 128-token blocks,
+    passed as 32-bit row words.  Flops count the kept 64-token tiles of the same
+    mask (the expanded form), as the headline metric does."""
+    import workloads
+    keep = workloads.mask_wan14b(w, block=128)
+    words = workloads.pack_bits32(keep)
+    wd = torch.from_numpy(words.view(np.int32)).to(qd.device)
+    m64 = bsa.mask_b128_to_b64(wd, w.seq_len)
+    kept = int(sum(int(x).bit_count() for x in m64.cpu().numpy().view(np.uint64).ravel()))
+    f = lambda: bsa.sparse_attn_b128(qd, kd, vd, wd, w.scale, out=out)
+    f()
+    ms = timed(f, 10)
+    print(json.dumps({"b128_layer": "Wan2.1-14B 720p, 128x128 blocks, 32-bit words",
+                      "density": round(float(keep.mean()), 4), "kept_64_tiles": kept, "ms": round(ms, 3),
+                      "tflops": round(kept * tile_flops(w.head_dim) / (ms * 1e-3) / 1e12, 1),
+                      "speedup_vs_full": round(ms_full / ms, 3)}), file=sys.stderr, flush=True)
 
 
 def aux_kernels(bsa, torch, timed):
@@ -288,11 +464,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline layer only (no other layers, top-p layer or density sweep)")
     ap.add_argument("--profile", action="store_true",
                     help="short run for counter collection: a few planned launches plus a 1 GiB copy")
-    ap.add_argument("--sweep", action="store_true", help="also run the density sweep (stderr)")
     ap.add_argument("--aux", action="store_true", help="also time the HBM-bound kernels (stderr)")
-    ap.add_argument("--topp", action="store_true", help="also time the dynamic top-p layer end to end (stderr)")
     ap.add_argument("--b128", action="store_true",
                     help="also time the layer under a 128x128-block mask in 32-bit words (stderr)")
     ap.add_argument("--cold", action="store_true",
@@ -317,26 +493,17 @@ def main():
     tb = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     qd, kd, vd = tb(q), tb(k), tb(v)
     md = torch.from_numpy(bits.view(np.int64)).to(dev)
-    full_bits = workloads.pack_bits(np.ones((1, w.n_blocks, w.n_blocks), bool))
-    fd = torch.from_numpy(np.repeat(full_bits, w.n_heads, axis=0).view(np.int64)).to(dev)
+    fd = full_mask(torch, w.n_heads, w.n_blocks, dev)
     out = torch.empty_like(qd)
     kept = int(keep.sum())
     flops = kept * tile_flops(w.head_dim)
     full_flops = w.n_heads * w.n_blocks ** 2 * tile_flops(w.head_dim)
     stream = torch.cuda.current_stream(dev)
+    timer = Timer(torch, stream)
+    print("[bench] inputs ready", file=sys.stderr, flush=True)
 
     def step(mask):
         bsa.sparse_attn(qd, kd, vd, mask, w.scale, out=out)
-
-    def timed(fn, n):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
 
     if args.profile:
         _, _, order = bsa.plan(md, w.seq_len)
@@ -352,19 +519,21 @@ def main():
 
     for _ in range(args.warmup):
         step(md)
-    ms = timed(lambda: step(md), args.steps)
-    print(f"[bench] sparse step {ms:.3f} ms", file=sys.stderr, flush=True)
+    ms, ms_med = timer.run(lambda: step(md), args.steps)
+    print(f"[bench] sparse step {ms:.3f} ms (median {ms_med:.3f})", file=sys.stderr, flush=True)
 
     for _ in range(max(1, args.warmup // 2)):
         step(fd)
-    ms_full = timed(lambda: step(fd), max(3, args.steps // 3))
+    ms_full = timer(lambda: step(fd), max(3, args.steps // 3))
     print(f"[bench] full-mask step {ms_full:.3f} ms", file=sys.stderr, flush=True)
 
     _, _, order = bsa.plan(md, w.seq_len)
     planned = lambda: bsa.sparse_attn(qd, kd, vd, md, w.scale, out=out, work_order=order)
     planned()
-    ms_k = timed(planned, args.steps)
+    ms_k = timer(planned, args.steps)
     achieved = flops / (ms_k * 1e-3) / 1e12
+    clock = gpu_clock_while(lambda: step(md))
+    print(f"[bench] clock {clock}", file=sys.stderr, flush=True)
 
     rec = {
         "metric": "effective bf16 TFLOP/s on kept blocks + speedup vs full mask, Wan-14B 720p shape",
@@ -374,6 +543,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "median_ms_per_step": round(ms_med, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -387,6 +557,7 @@ def main():
             "parallelism": "single GPU",
         },
         "speedup_vs_full_mask": round(ms_full / ms, 3),
+        "ideal_speedup": round(w.n_heads * w.n_blocks ** 2 / kept, 3),
         "full_mask_ms": round(ms_full, 4),
         "full_mask_tflops": round(full_flops / (ms_full * 1e-3) / 1e12, 3),
         "roofline": {
@@ -399,19 +570,27 @@ def main():
             "kernel": "attn_pair_kernel<128> (pair rows) + attn_fwd_bf16_kernel<128> (single rows), one planned call",
             "kernel_ms": round(ms_k, 4),
         },
+        "gpu_clock": clock,
     }
-    if args.sweep:
-        density_sweep(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
     if args.aux:
-        aux_kernels(bsa, torch, timed)
-    if args.topp:
-        topp_layer(bsa, torch, timed)
+        aux_kernels(bsa, torch, timer)
     if args.b128:
-        b128_layer(bsa, torch, w, qd, kd, vd, out, timed, ms_full)
+        b128_layer(bsa, torch, w, qd, kd, vd, out, timer, ms_full)
     if args.cold:
         cold_steps(torch, lambda: step(md), stream, max(5, args.steps), ms)
     if args.ceiling:
-        gemm_ceiling(torch, timed, achieved)
+        gemm_ceiling(torch, timer, achieved)
+    if not args.quick:
+        rec["density_sweep"] = density_sweep(bsa, torch, w, qd, kd, vd, out, timer, ms_full)
+    del qd, kd, vd, out, md, fd
+    torch.cuda.empty_cache()
+    if not args.quick:
+        rec["wan13b_480p"] = static_layer(bsa, torch, "wan13b_480p", timer, args.steps)
+        torch.cuda.empty_cache()
+        rec["hunyuan_768"] = hunyuan_layer(bsa, torch, timer, args.steps)
+        torch.cuda.empty_cache()
+        rec["topp_wan14b"] = topp_layer(bsa, torch, timer)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, bits, keep)
     else:
