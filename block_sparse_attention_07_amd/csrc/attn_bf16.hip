@@ -61,10 +61,37 @@ constexpr int BLK = 64;
 constexpr int NT = 256;
 constexpr int LIST_CAP = 2048;
 constexpr int CHUNK_WORDS = LIST_CAP / 64;
+// Softmax rescaling is checked on each lane's row sum of a tile's 16 bf16
+// probabilities, taken against the running max (exp2 domain): while it stays
+// at or below 2^20 no probability exceeds 2^20, and O and l cannot overflow
+// (2^20 times any key count and value scale here is far below the fp32 range).
+// A larger, infinite or NaN sum sends the step to the rescale path.
+constexpr float SUM_LIMIT = 1048576.0f;
+// Single rows keep the running max: it moves only when a tile's max exceeds it
+// by more than this (a factor 2^8 in probability).
 constexpr float RESCALE_SLACK = 8.0f;
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family GPUs:
 // 32-bit data format, so the per-access range check against num_records applies.
 constexpr int BUFFER_DWORD3 = 0x00020000;
+
+// Rounds a tile-half's 16 probabilities to the bf16 B operands of the PV MFMAs
+// and sums the rounded values (the weights PV uses) with two-way dot products
+// against (1, 1).
+__device__ __forceinline__ void to_bf16_sum(const float (&p)[16], bf16x8& pb0, bf16x8& pb1, float& ls) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pb0[j] = (__bf16)p[j];
+    pb1[j] = (__bf16)p[8 + j];
+  }
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb0[2 * j], pb0[2 * j + 1]}, one, ls0, false);
+    ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb1[2 * j], pb1[2 * j + 1]}, one, ls1, false);
+  }
+  ls = ls0 + ls1;
+}
 
 // Key order inside a tile.  K row r holds key key_of_row(r): r with bits 2 and
 // 3 exchanged.  The QK^T accumulator register i of lane l (query l % 32) then
@@ -661,30 +688,10 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
         }
       }
     }
-    float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
-#pragma unroll
-    for (int i = 2; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s0[i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s1[i]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt = mx * c;
-    if (__any(mt > m_run + RESCALE_SLACK)) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m_run = mn;
-    }
-    // key half 0: next tile's QK^T interleaved with this tile's exp2, then half 1
+    // key half 0: next tile's QK^T interleaved with this tile's exp2, then half 1;
+    // exponentials against the running max as it stands (see the single-row step)
     bf16x8 pb[2][2];
-    float lsum = 0.f;
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float lh[2];
     f32x16 sn[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -708,16 +715,7 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
         p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
         p[i + 1] = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -m_run));
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pb[kh][0][j] = (__bf16)p[j];
-        pb[kh][1][j] = (__bf16)p[8 + j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[kh][0][2 * j], pb[kh][0][2 * j + 1]}, one, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[kh][1][2 * j], pb[kh][1][2 * j + 1]}, one, lsum, false);
-      }
+      to_bf16_sum(p, pb[kh][0], pb[kh][1], lh[kh]);
       __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -725,7 +723,32 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
     }
-    l_part += lsum;
+    if (__any(!(lh[0] <= SUM_LIMIT && lh[1] <= SUM_LIMIT))) {
+      float mx = __builtin_elementwise_maximum(s0[0], s0[1]);
+#pragma unroll
+      for (int i = 2; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s0[i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s1[i]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const float mn = fmaxf(m_run, mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_run = mn;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const f32x16& s = kh ? s1 : s0;
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m_run));
+        to_bf16_sum(p, pb[kh][0], pb[kh][1], lh[kh]);
+      }
+    }
+    l_part += lh[0] + lh[1];
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
