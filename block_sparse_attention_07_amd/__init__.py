@@ -29,6 +29,7 @@ from .api import (  # noqa: F401
     plan,
     sparse_attn,
     sparse_attn_b128,
+    sparse_attn_noalloc,
     threshold_map_resize,
     workspace_bytes,
 )

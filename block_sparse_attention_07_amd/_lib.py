@@ -19,6 +19,7 @@ _f = ctypes.c_float
 SIGNATURES = {
     "bsa_mask_words": [_i, _i],
     "sparse_attn_fwd": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],
+    "sparse_attn_fwd_noalloc": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],
     "sparse_attn_workspace_bytes": [_i, _i, _i],
     "sparse_attn_fwd_ws": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, ctypes.c_size_t, _p],
     "sparse_attn_fwd_f32": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p],

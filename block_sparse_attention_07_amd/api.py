@@ -123,6 +123,27 @@ def sparse_attn(q, k, v, mask_bits, scale=None, out=None, work_order=None, works
     return out
 
 
+@_on_device
+def sparse_attn_noalloc(q, k, v, mask_bits, scale=None, out=None):
+    """bf16 block-sparse attention through sparse_attn_fwd_noalloc: the library's
+    scratch is its fixed device array, nothing is allocated inside the call (pass
+    ``out`` to keep the binding from allocating the output)."""
+    _dev(q, k, v, mask_bits)
+    _need(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must share shape [H, N, d]")
+    _need(q.dtype == k.dtype == v.dtype == torch.bfloat16, "q, k, v must be bfloat16")
+    H, N, d = q.shape
+    _check_mask(mask_bits, H, N)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(q, out)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    rc = lib().sparse_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(mask_bits), H, N, d, BLOCK, BLOCK,
+                                       scale, _ptr(out), _stream(q))
+    check(rc, "sparse_attn_fwd_noalloc")
+    return out
+
+
 def _check_mask32(mask_words, H, N):
     nb = -(-N // 128)
     W = -(-nb // 32)

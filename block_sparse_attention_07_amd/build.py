@@ -36,6 +36,7 @@ SOURCES = [
     "fidelity.hip",
     "resize.hip",
     "b128.hip",
+    "noalloc.hip",
 ]
 EXTRA_FLAGS = {"topp.hip": ["-ffp-contract=off"]}
 

@@ -952,9 +952,15 @@ AttnWorkspace attn_workspace(int n_heads, int seq_len, int head_dim) {
   w.bytes = w.off_vt + vt_bytes(n_heads, seq_len, head_dim);
   return w;
 }
-int attn_with_workspace(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
-                        int n_heads, int seq_len, int head_dim, float scale, void* out, char* ws,
-                        hipStream_t stream) {
+}  // namespace
+
+size_t attn_workspace_bytes(int n_heads, int seq_len, int head_dim) {
+  return attn_workspace(n_heads, seq_len, head_dim).bytes;
+}
+
+int attn_bf16_with_workspace(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                             int n_heads, int seq_len, int head_dim, float scale, void* out, char* ws,
+                             hipStream_t stream) {
   const AttnWorkspace w = attn_workspace(n_heads, seq_len, head_dim);
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   int64_t* tiles = reinterpret_cast<int64_t*>(ws + w.off_tiles);
@@ -964,7 +970,6 @@ int attn_with_workspace(const void* q, const void* k, const void* v, const uint6
   return launch_attn_bf16(q, k, v, mask_bits, order, n_heads, seq_len, head_dim, scale, out,
                           ws + w.off_vt, stream);
 }
-}  // namespace
 }  // namespace bsa
 
 extern "C" int sparse_attn_fwd(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
@@ -977,7 +982,7 @@ extern "C" int sparse_attn_fwd(const void* q, const void* k, const void* v, cons
   ScratchLease lease(attn_workspace(n_heads, seq_len, head_dim).bytes);
   char* ws = static_cast<char*>(lease.get());
   if (!ws) return BSA_ERR_HIP;
-  return attn_with_workspace(q, k, v, mask_bits, n_heads, seq_len, head_dim, scale, out, ws, stream);
+  return attn_bf16_with_workspace(q, k, v, mask_bits, n_heads, seq_len, head_dim, scale, out, ws, stream);
 }
 
 extern "C" size_t sparse_attn_workspace_bytes(int n_heads, int seq_len, int head_dim) {
@@ -1001,8 +1006,8 @@ extern "C" int sparse_attn_fwd_ws(const void* q, const void* k, const void* v,
   if (workspace_bytes < need)
     return fail(BSA_ERR_INVALID_ARG, "workspace holds %zu bytes, this call needs %zu", workspace_bytes,
                 need);
-  return attn_with_workspace(q, k, v, mask_bits, n_heads, seq_len, head_dim, scale, out,
-                             static_cast<char*>(workspace), stream);
+  return attn_bf16_with_workspace(q, k, v, mask_bits, n_heads, seq_len, head_dim, scale, out,
+                                  static_cast<char*>(workspace), stream);
 }
 
 extern "C" int sparse_attn_fwd_planned(const void* q, const void* k, const void* v,

@@ -55,6 +55,13 @@ int launch_plan(const uint64_t* mask, int n_heads, int seq_len, int32_t* counts,
 
 // Bytes of the transposed-V workspace the bf16 attention path needs.
 size_t vt_bytes(int n_heads, int seq_len, int head_dim);
+// Bytes of the workspace of the unplanned bf16 attention (plan + transposed V,
+// 256-byte aligned parts), and that attention run on a given workspace
+// (attn_bf16.hip).
+size_t attn_workspace_bytes(int n_heads, int seq_len, int head_dim);
+int attn_bf16_with_workspace(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                             int n_heads, int seq_len, int head_dim, float scale, void* out, char* ws,
+                             hipStream_t stream);
 // Launch the bf16 attention path (V transpose into `vt`, then the attention
 // kernel) with an optional work order (attn_bf16.hip).
 int launch_attn_bf16(const void* q, const void* k, const void* v, const uint64_t* mask,

@@ -117,6 +117,23 @@ int sparse_attn_fwd_ws(const void* q, const void* k, const void* v, const uint64
                        hipStream_t stream);
 
 /*
+ * sparse_attn_fwd_noalloc -- sparse_attn_fwd for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, same result bit for bit.  Its scratch memory (plan +
+ * transposed V) is one fixed 256 MiB array in the library's code object, which every
+ * device the library runs on holds until the process ends; the call itself allocates,
+ * frees and synchronises nothing.  The heads go through in chunks whose scratch fits
+ * the array (a multiple of 4 heads when at least 4 fit), one after another on `stream`.
+ * A shape whose single head needs more than the array (about 1M tokens at
+ * head_dim 128) is BSA_ERR_UNSUPPORTED, returned before any HIP call.  Every call on a
+ * device shares that device's array and leaves its contents behind (each call rewrites
+ * all it reads), so calls whose kernels overlap on one device race on it.
+ */
+int sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, const uint64_t* mask_bits,
+                            int n_heads, int seq_len, int head_dim, int block_q, int block_k,
+                            float scale, void* out, hipStream_t stream);
+
+/*
  * sparse_attn_fwd_f32 -- same operation and arguments with fp32 q, k, v, out and
  * fp32 arithmetic throughout (reference-precision path for small cases).
  */

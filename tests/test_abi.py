@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(names) == sorted(_lib.EXPORTS)
 
 
@@ -55,6 +55,17 @@ def test_workspace_argument_errors_precede_any_device_call(ws, nbytes):
     w = ctypes.c_void_p(ws) if ws else None
     assert L.sparse_attn_fwd_ws(*a[:11], w, nbytes, None) == 1
     assert L.bsa_last_error().decode()
+
+
+def test_noalloc_rejects_a_head_larger_than_its_array_before_any_device_call():
+    """One head whose plan and transposed V exceed the fixed 256 MiB array (2^20 + 64
+    tokens at head_dim 128) is refused on the host; so are the usual argument errors."""
+    L = _lib.lib()
+    a = list(_attn_args(N=(1 << 20) + 64, d=128, H=1))
+    assert L.sparse_attn_fwd_noalloc(*a) == 2
+    assert "fixed array" in L.bsa_last_error().decode()
+    assert L.sparse_attn_fwd_noalloc(*_attn_args(q=0)) == 1
+    assert L.sparse_attn_fwd_noalloc(*_attn_args(d=96)) == 2
 
 
 def test_mask_words():
