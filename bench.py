@@ -16,7 +16,7 @@ Reported on one JSON line:
   value      effective TFLOP/s on kept blocks = kept tiles * 4*64*64*128 / step time
              (mean over the K timed steps); median_ms_per_step from per-step events
   speedup_vs_full_mask   step time with an all-ones mask / step time with the workload mask
-  roofline   one planned call of the attention path (V transpose, pair launch,
+  roofline   one planned call of the attention path (V transpose, pairs plus first slices,
              single-row slices; events on its stream): algorithmic flops per call /
              average call time vs the bf16 MFMA peak
   cpu_baseline  the float64 CPU oracle on a bounded sample of query blocks

@@ -40,7 +40,10 @@
 //  * With a work order, single rows go out one device-full of workgroups per
 //    launch so that rows of similar length start together and walk their tile
 //    lists in step; within a launch the XCDs are split into groups that walk
-//    different heads (see the row decode in attn_fwd_bf16_kernel).
+//    different heads (see the row decode in single_row_body).  The pair
+//    workgroups and the first few single-row slices share one launch
+//    (attn_mixed_kernel), so single rows fill the slots the pairs' last,
+//    partial round leaves idle.
 #include <cmath>
 #include <type_traits>
 
@@ -152,10 +155,11 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const u16* __restrict_
 
 // Single rows: one 64-query row per workgroup of 4 waves, two workgroups per CU.
 template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
+__device__ __forceinline__ void single_row_body(
+    int wg, const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int stream_off,
-    int groups, int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
+    int groups, int n_heads, int N, int nb, int W, float c, u16* __restrict__ O,
+    u16* __restrict__ kst0, u16* __restrict__ kst1, u16* __restrict__ vts0, u16* __restrict__ vts1, u16* __restrict__ list, int& nlist) {
   constexpr int CPR = D / 8;             // 16-byte chunks per token row
   constexpr int NDB = D / 32;            // 32-wide output column blocks
   constexpr int NKS = D / 16;            // k-steps of the QK^T contraction
@@ -165,12 +169,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   // where its own stage is read.  After the tile loop the V^T stages hold the
   // merge of the two key halves' accumulators and the list their running max
   // and sum.
-  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];   // K stage 0; row r holds key_of_row(r)
-  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];   // K stage 1
-  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];   // V^T stage 0; row d holds 64 keys
-  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];   // V^T stage 1
-  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
-  __shared__ int nlist;
+  // (K stages: row r holds key_of_row(r); V^T stages: row d holds 64 keys)
   auto kstage = [&](int b) { return b ? kst1 : kst0; };
   auto vstage = [&](int b) { return b ? vts1 : vts0; };
 
@@ -194,9 +193,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   // a head are fetched into the L2s of 8 / groups XCDs instead of all eight.
   // With groups == 1 slot stream_off + blockIdx.x is taken (any grid size).
   const int total_rows = n_heads * nb;
-  int row_id = blockIdx.x;
+  int row_id = wg;
   if (order) {
-    const int i = blockIdx.x, x = i & 7, g = x % groups;
+    const int i = wg, x = i & 7, g = x % groups;
     const int p = stream_off + x / groups + (8 / groups) * (i >> 3);
     const int r = g + groups * (p / nb);
     if (r >= n_heads) return;
@@ -506,8 +505,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   // Merge the two key halves of each query-row half and write the output.
   // mo(j)[accumulator register][lane], j = rh, overlays a V^T stage (each
   // 128 * D bytes); mm / ml overlay the block list.
-  static_assert(sizeof(vts0) == (D / 2) * 64 * sizeof(float), "merge overlay size");
-  static_assert(sizeof(list) >= 2 * 2 * 32 * sizeof(float), "merge overlay size");
+  static_assert(D * BLK * sizeof(u16) == (D / 2) * 64 * sizeof(float), "merge overlay size");
+  static_assert(LIST_CAP * sizeof(u16) >= 2 * 2 * 32 * sizeof(float), "merge overlay size");
   auto mo = [&](int j) { return reinterpret_cast<float (*)[64]>(j ? vts1 : vts0); };
   const int mj = rh;
   auto mm = reinterpret_cast<float (*)[32]>(list);
@@ -562,19 +561,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 // once for 128 queries, and the workgroup is as small as a single-row one: two
 // of them share a CU and each SIMD runs one wave of each, which are not in step.
 template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
+__device__ __forceinline__ void pair_body(
+    int wg, const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
     const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int n_heads, int N,
-    int nb, int W, float c, u16* __restrict__ O) {
+    int nb, int W, float c, u16* __restrict__ O, u16* __restrict__ kst0, u16* __restrict__ kst1, u16* __restrict__ vts0, u16* __restrict__ vts1, u16* __restrict__ list, int& nlist) {
   constexpr int CPR = D / 8;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];
-  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];
-  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];
-  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];
-  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
-  __shared__ int nlist;
   auto kstage = [&](int b) { return b ? kst1 : kst0; };
   auto vstage = [&](int b) { return b ? vts1 : vts0; };
 
@@ -588,7 +581,7 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
 
   const int total_rows = n_heads * nb;
   const int half = nb >> 1;
-  const int e = order[(blockIdx.x / half) * nb + (blockIdx.x % half)];
+  const int e = order[(wg / half) * nb + (wg % half)];
   if (e < total_rows || e >= 2 * total_rows) return;
   const int row_id = e - total_rows;
   if ((row_id % nb) & 1 || (row_id % nb) + 1 >= nb) return;
@@ -624,14 +617,20 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
   constexpr int KR = 1024 / (2 * D);
   constexpr int NI = D / 32;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  int k_voff[NI], v_voff[NI];
+  // V^T copy offsets: instruction i fills V^T rows 8 (NI w + i) .. +7; at d = 128
+  // instructions i and i + 2 differ only by 16 rows (the swizzle repeats), which
+  // the scalar offset carries, so two registers hold all four lane offsets.
+  constexpr int NVO = NI >= 4 ? 2 : NI;
+  int k_voff[NI], v_voff[NVO];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int ii = wave_u * NI + i;
     const int r = ii * KR + lane / CPR;
     k_voff[i] = (key_of_row(r) * CPR + ((lane % CPR) ^ k_swz<D>(r))) * 16;
-    const int d = 8 * ii + (lane >> 3);
-    v_voff[i] = d * (int)npad * 2 + 16 * ((lane & 7) ^ v_swz(d));
+    if (i < NVO) {
+      const int d = 8 * ii + (lane >> 3);
+      v_voff[i] = d * (int)npad * 2 + 16 * ((lane & 7) ^ v_swz(d));
+    }
   }
   // K operand offsets of key half 0 (rows r32); half 1 is 32 rows further.
   int k_rd[NKS];
@@ -657,7 +656,7 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           vrs, (__attribute__((address_space(3))) void*)(vstage(vbuf) + (wave_u * NI + i) * 8 * BLK), 16,
-          v_voff[i], vvb * BLK * 2, 0, 0);
+          v_voff[i % NVO], vvb * BLK * 2 + (i / NVO) * 32 * (int)npad, 0, 0);
 #endif
   };
   auto kread = [&](int kbuf, int kh, int ks) {
@@ -826,9 +825,10 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
 
   // Each wave holds whole rows (both key halves): lanes l and l ^ 32 hold the two
   // key parities of each row's sum.
-  const float l_row = l_part + __shfl_xor(l_part, 32);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+  const float l_row = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
-  const int row = BLK * (u + qb) + 32 * rh + r32;
+  const int row = BLK * (u + qb) + 32 * rh + (int)(__lane_id() & 31);
   if (row < N) {
     u16* orow = O + head_off + (size_t)row * D;
 #pragma unroll
@@ -841,6 +841,70 @@ __global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
         *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * q4 + 4 * g) = y;
       }
   }
+}
+
+
+// The kernels: single rows, pair rows, and one launch holding the pair
+// workgroups followed by the first single-row slices (attn_mixed_kernel), so
+// that single rows take the slots the pair launch's last, partial round leaves
+// free.  All three declare the same LDS objects.
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int stream_off,
+    int groups, int n_heads, int N, int nb, int W, float c, u16* __restrict__ O) {
+  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
+  __shared__ int nlist;
+  single_row_body<D>(blockIdx.x, Q, K, VT, mask, order, stream_off, groups, n_heads, N, nb, W, c, O,
+                     kst0, kst1, vts0, vts1, list, nlist);
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int n_heads, int N,
+    int nb, int W, float c, u16* __restrict__ O) {
+  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
+  __shared__ int nlist;
+  pair_body<D>(blockIdx.x, Q, K, VT, mask, order, n_heads, N, nb, W, c, O, kst0, kst1, vts0, vts1, list, nlist);
+}
+
+// Workgroups [0, pair_wgs) are the pair launch (pair_wgs a multiple of 8; those
+// past n_heads * (nb / 2) exit); the rest are single-row slices of slice_wgs
+// workgroups each (a multiple of 8 when groups > 1), so every workgroup keeps
+// its XCD (workgroup index mod 8) in the slice's layout.
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_mixed_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
+    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int pair_wgs,
+    int slice_wgs, int stream_off, int groups, int n_heads, int N, int nb, int W, float c,
+    u16* __restrict__ O) {
+  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];
+  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];
+  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
+  __shared__ int nlist;
+  const int b = blockIdx.x;
+  if (b < pair_wgs) {
+    if (b < n_heads * (nb / 2))
+      pair_body<D>(b, Q, K, VT, mask, order, n_heads, N, nb, W, c, O, kst0, kst1, vts0, vts1, list, nlist);
+    return;
+  }
+  const int j = b - pair_wgs;
+  if (groups > 1)
+    single_row_body<D>(j % slice_wgs, Q, K, VT, mask, order, stream_off + (j / slice_wgs) * (slice_wgs / groups),
+                       groups, n_heads, N, nb, W, c, O, kst0, kst1, vts0, vts1, list, nlist);
+  else
+    single_row_body<D>(j, Q, K, VT, mask, order, stream_off, 1, n_heads, N, nb, W, c, O, kst0, kst1, vts0, vts1, list, nlist);
 }
 
 // Workgroups the device holds at once for this kernel (CUs x resident
@@ -876,22 +940,36 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   // and the tiles in use then spread over the whole head.  Within a slice the
   // XCDs are split into groups that work on different heads (see the kernel's
   // row decode).  Without an order the grid goes out in one launch.
-  // Pair entries (two query blocks with identical mask rows) go first, in one
-  // launch of 128-query workgroups over the pair slots of every head segment.
+  // Pair entries (two query blocks with identical mask rows) go first, as
+  // 128-query workgroups over the pair slots of every head segment.  They are
+  // all the same length (a full head's pair row walks every tile), so their last
+  // round is partial; the first MIX single-row slices ride in the same launch,
+  // after the pair workgroups, and take those idle slots (a whole launch of
+  // 4728 pairs at the Wan2.1-14B shape leaves about 1 ms of the layer idle).
   const int total = n_heads * nb;
-  if (order && nb >= 2) {
-    hipLaunchKernelGGL((attn_pair_kernel<D>), dim3((unsigned)(n_heads * (nb / 2))), dim3(NT), 0, stream, Q, K,
-                       VT, mask, order, n_heads, seq_len, nb, W, c, O);
-    BSA_CHECK_HIP(hipGetLastError());
-  }
   int gen = order ? generation_size<D>() : 0;
   if (gen <= 0) gen = total;
   // XCD groups for the single-row slices: 4 when the heads split evenly over
   // four streams, else 2 or 1; a slice must be a whole number of rounds of 8.
   int groups = 1;
   if (order && gen % 8 == 0) groups = n_heads % 4 == 0 ? 4 : (n_heads % 2 == 0 ? 2 : 1);
+  const int per = gen / groups;                 // slots of each stream per slice
+  const int len = (n_heads / groups) * nb;      // slots in each stream
+  // Pair entries go first, in the same launch as the first MIX single-row
+  // slices (see attn_mixed_kernel); the remaining slices follow one launch each.
+  constexpr int MIX = 4;
+  int first = 0;                                // first slice not yet launched
+  if (order && nb >= 2) {
+    const int pair_wgs = (n_heads * (nb / 2) + 7) & ~7;
+    const int slices = groups == 1 ? (total + gen - 1) / gen : (len + per - 1) / per;
+    first = slices < MIX ? slices : MIX;
+    const int singles = groups == 1 ? (first * gen < total ? first * gen : total) : first * gen;
+    hipLaunchKernelGGL((attn_mixed_kernel<D>), dim3((unsigned)(pair_wgs + singles)), dim3(NT), 0, stream, Q,
+                       K, VT, mask, order, pair_wgs, gen, 0, groups, n_heads, seq_len, nb, W, c, O);
+    BSA_CHECK_HIP(hipGetLastError());
+  }
   if (groups == 1) {
-    for (int off = 0; off < total; off += gen) {
+    for (int off = first * gen; off < total; off += gen) {
       const int count = min(gen, total - off);
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
                          mask, order, off, 1, n_heads, seq_len, nb, W, c, O);
@@ -899,9 +977,7 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
     }
     return ok();
   }
-  const int per = gen / groups;                 // slots of each stream per slice
-  const int len = (n_heads / groups) * nb;      // slots in each stream
-  for (int off = 0; off < len; off += per) {
+  for (int off = first * per; off < len; off += per) {
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)gen), dim3(NT), 0, stream, Q, K, VT,
                        mask, order, off, groups, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());
