@@ -41,9 +41,9 @@
 //    launch so that rows of similar length start together and walk their tile
 //    lists in step; within a launch the XCDs are split into groups that walk
 //    different heads (see the row decode in single_row_body).  The pair
-//    workgroups and the first few single-row slices share one launch
-//    (attn_mixed_kernel), so single rows fill the slots the pairs' last,
-//    partial round leaves idle.
+//    workgroups and the last few single-row slices (the lightest heads' rows)
+//    share one launch (attn_mixed_kernel), so single rows fill the slots the
+//    pairs' last, partial round leaves idle.
 #include <cmath>
 #include <type_traits>
 
@@ -845,7 +845,7 @@ __device__ __forceinline__ void pair_body(
 
 
 // The kernels: single rows, pair rows, and one launch holding the pair
-// workgroups followed by the first single-row slices (attn_mixed_kernel), so
+// workgroups followed by the last single-row slices (attn_mixed_kernel), so
 // that single rows take the slots the pair launch's last, partial round leaves
 // free.  All three declare the same LDS objects.
 template <int D>
@@ -943,7 +943,7 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   // Pair entries (two query blocks with identical mask rows) go first, as
   // 128-query workgroups over the pair slots of every head segment.  They are
   // all the same length (a full head's pair row walks every tile), so their last
-  // round is partial; the first MIX single-row slices ride in the same launch,
+  // round is partial; the last MIX single-row slices ride in the same launch,
   // after the pair workgroups, and take those idle slots (a whole launch of
   // 4728 pairs at the Wan2.1-14B shape leaves about 1 ms of the layer idle).
   const int total = n_heads * nb;
@@ -955,21 +955,26 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   if (order && gen % 8 == 0) groups = n_heads % 4 == 0 ? 4 : (n_heads % 2 == 0 ? 2 : 1);
   const int per = gen / groups;                 // slots of each stream per slice
   const int len = (n_heads / groups) * nb;      // slots in each stream
-  // Pair entries go first, in the same launch as the first MIX single-row
-  // slices (see attn_mixed_kernel); the remaining slices follow one launch each.
-  constexpr int MIX = 4;
-  int first = 0;                                // first slice not yet launched
+  // Pair entries go first, in the same launch as the last MIX single-row slices
+  // (see attn_mixed_kernel): those hold the lightest heads' rows, which are
+  // short, and hold rows at all unless every row of those heads is paired (the
+  // heads whose rows are all paired are the full ones, which rank first by total
+  // work, so their empty single-row slots are the first slices).  The other
+  // slices follow one launch each, heaviest first.
+  constexpr int MIX = 8;
+  const int slices = groups == 1 ? (total + gen - 1) / gen : (len + per - 1) / per;
+  int last = slices;                            // slices [last, slices) ride with the pairs
   if (order && nb >= 2) {
     const int pair_wgs = (n_heads * (nb / 2) + 7) & ~7;
-    const int slices = groups == 1 ? (total + gen - 1) / gen : (len + per - 1) / per;
-    first = slices < MIX ? slices : MIX;
-    const int singles = groups == 1 ? (first * gen < total ? first * gen : total) : first * gen;
+    last = slices > MIX ? slices - MIX : 0;
+    const int off = groups == 1 ? last * gen : last * per;
+    const int singles = groups == 1 ? total - off : (slices - last) * gen;
     hipLaunchKernelGGL((attn_mixed_kernel<D>), dim3((unsigned)(pair_wgs + singles)), dim3(NT), 0, stream, Q,
-                       K, VT, mask, order, pair_wgs, gen, 0, groups, n_heads, seq_len, nb, W, c, O);
+                       K, VT, mask, order, pair_wgs, gen, off, groups, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());
   }
   if (groups == 1) {
-    for (int off = first * gen; off < total; off += gen) {
+    for (int off = 0; off < last * gen && off < total; off += gen) {
       const int count = min(gen, total - off);
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)count), dim3(NT), 0, stream, Q, K, VT,
                          mask, order, off, 1, n_heads, seq_len, nb, W, c, O);
@@ -977,7 +982,7 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
     }
     return ok();
   }
-  for (int off = first * per; off < len; off += per) {
+  for (int off = 0; off < last * per && off < len; off += per) {
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)gen), dim3(NT), 0, stream, Q, K, VT,
                        mask, order, off, groups, n_heads, seq_len, nb, W, c, O);
     BSA_CHECK_HIP(hipGetLastError());

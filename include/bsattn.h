@@ -174,9 +174,9 @@ int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int bl
  * library's per-device scratch buffer (see sparse_attn_fwd about overlapping calls).
  * After the transpose, the single entries go out in slices of one device-full of
  * workgroups each (compute units x resident workgroups per unit), so that the rows of each
- * slice start together.  The pair entries share one launch with the first four slices
- * (pair workgroups first, the slices behind them); the rest of the slices are
- * consecutive kernel launches.  The
+ * slice start together.  The pair entries share one launch with the last eight slices
+ * (pair workgroups first, the slices behind them: the lightest rows, which fill the
+ * pairs' last round); the other slices follow as consecutive kernel launches.  The
  * XCDs are split into G groups (G = 4 when n_heads is a multiple of 4, else 2 when it
  * is even, else 1): group g walks the segments g, g + G, g + 2G, ... back to back, and
  * each launch takes the next device-full / G slots of every group's walk, so the K/V
