@@ -16,8 +16,8 @@ Reported on one JSON line:
   value      effective TFLOP/s on kept blocks = kept tiles * 4*64*64*128 / step time
              (mean over the K timed steps); median_ms_per_step from per-step events
   speedup_vs_full_mask   step time with an all-ones mask / step time with the workload mask
-  roofline   one planned call of the attention path (V transpose, pairs plus first slices,
-             single-row slices; events on its stream): algorithmic flops per call /
+  roofline   one planned call of the attention path (V transpose, pairs plus the last
+             single-row slices, the other slices; events on its stream): algorithmic flops per call /
              average call time vs the bf16 MFMA peak
   cpu_baseline  the float64 CPU oracle on a bounded sample of query blocks
   wan13b_480p, hunyuan_768   the other layer shapes, each with its step time,
@@ -35,12 +35,17 @@ Reported on one JSON line:
          block scores, top-p, permutation, resize, fidelity) in GB/s vs 8 TB/s.
 --b128   (extra, to stderr) the same layer under the same mask recipe drawn over
          128x128-token blocks and passed as 32-bit row words (ScalingAttention's CRM format).
---cold   (extra, to stderr) steps timed one by one after a 512 MiB device write that
-         evicts the 256 MB last-level cache (MALL), median against back-to-back steps.
-mfma_ceiling  (default run; with --quick only under --ceiling) a reference point for the
-         roofline, not part of the path: a dense bf16 GEMM from the vendor library
-         (torch.matmul) at 8192^3 and 16384^3 on the same GPU, and the headline and
-         all-ones rates as fractions of the best of them.
+cold     (default run; with --quick only under --cold) steps timed one by one after a
+         512 MiB device write that evicts the 256 MB last-level cache (MALL), median
+         against the median of the back-to-back steps.
+dense_sdpa  (default run) dense attention at the headline shape from PyTorch's fused
+         kernels (flash / memory-efficient backend, never the math backend), and how much
+         faster the all-ones and workload masks run here: context, not part of the path.
+mfma_ceiling  (default run; with --quick only under --ceiling) reference points for the
+         roofline, not part of the path, measured on the same GPU: the library's
+         register-only MFMA probe (bsa_mfma_probe) and a dense bf16 GEMM from the vendor
+         library (torch.matmul) at 8192^3 and 16384^3, with the headline and all-ones
+         rates as fractions of each.
 """
 from __future__ import annotations
 
@@ -421,11 +426,20 @@ def aux_kernels(bsa, torch, timed):
            ms_out.numel() * 8)
 
 
-def gemm_ceiling(torch, timed):
-    """A dense bf16 GEMM from the vendor library, timed on the same GPU in the same
-    run: the practical MFMA rate at the clock this chip holds under a dense
-    contraction (context for the roofline fraction, not part of the path)."""
+def gemm_ceiling(bsa, torch, timed):
+    """Two practical MFMA ceilings on the same GPU in the same run (context for the
+    roofline fraction, not part of the path): the library's register-only MFMA
+    probe (the issue rate at the clock the chip holds under MFMA load) and a dense
+    bf16 GEMM from the vendor library."""
     dev = torch.device("cuda", 0)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(512 * cus, dtype=torch.float32, device=dev)
+    bsa.mfma_probe(sink, 2000)
+    iters = 100000
+    probe_flops = bsa.mfma_probe(sink, iters)
+    ms = timed(lambda: bsa.mfma_probe(sink, iters), 2)
+    probe = round(probe_flops / (ms * 1e-3) / 1e12, 1)
+    del sink
     sizes = {}
     for n in (8192, 16384):
         a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
@@ -437,12 +451,36 @@ def gemm_ceiling(torch, timed):
         sizes[str(n)] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
         del a, b, c
     torch.cuda.empty_cache()
-    return {"kind": "vendor bf16 GEMM n^3 (torch.matmul, vendor BLAS), same GPU and run",
-            "tflops_by_n": sizes, "best_tflops": max(sizes.values())}
+    return {"mfma_probe_tflops": probe,
+            "mfma_probe": "bsa_mfma_probe: 16 bf16 32x32x16 MFMAs per wave and iteration on "
+                          "register operands, 2 x 4-wave workgroups per CU, no memory traffic",
+            "gemm_kind": "vendor bf16 GEMM n^3 (torch.matmul, vendor BLAS)",
+            "gemm_tflops_by_n": sizes, "gemm_best_tflops": max(sizes.values())}
+
+
+def dense_sdpa(torch, timed, qd, kd, vd, ms_sparse, ms_full):
+    """Dense attention at the same shape from PyTorch's fused kernels (flash or
+    memory-efficient backend; the math backend, which would materialise every
+    score, is never allowed): context for the all-ones mask, not part of the path."""
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+    H, N, d = qd.shape
+    q, k, v = (x.view(1, H, N, d) for x in (qd, kd, vd))
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            fn = lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            fn()
+            ms = timed(fn, 3)
+    except (RuntimeError, NotImplementedError) as ex:
+        return {"available": False, "reason": str(ex)[:160]}
+    torch.cuda.empty_cache()
+    return {"kind": "torch scaled_dot_product_attention, fused backend, every key kept, same shape",
+            "ms": round(ms, 3), "tflops": round(4 * H * N * N * d / (ms * 1e-3) / 1e12, 1),
+            "all_ones_mask_speedup": round(ms / ms_full, 3), "workload_speedup": round(ms / ms_sparse, 3)}
 
 
 def cold_steps(torch, fn, stream, n, ms_warm):
-    """Median single-step time after a 512 MiB write that evicts the 256 MB MALL."""
+    """Median single-step time after a 512 MiB write that evicts the 256 MB MALL,
+    next to the median of the back-to-back (warm) steps."""
     junk = torch.empty(1 << 28, dtype=torch.int16, device=stream.device)
     times = []
     for _ in range(n):
@@ -454,15 +492,17 @@ def cold_steps(torch, fn, stream, n, ms_warm):
         e1.record(stream)
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
+    del junk
     times.sort()
-    print(json.dumps({"cold_step_ms": round(times[len(times) // 2], 3), "steps": n,
-                      "warm_step_ms": round(ms_warm, 3)}), file=sys.stderr, flush=True)
+    return {"cold_median_ms": round(times[len(times) // 2], 3), "steps": n,
+            "warm_median_ms": round(ms_warm, 3),
+            "evict": "512 MiB device write before each step (the MALL holds 256 MB)"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=25)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true",
@@ -577,12 +617,15 @@ def main():
         aux_kernels(bsa, torch, timer)
     if args.b128:
         b128_layer(bsa, torch, w, qd, kd, vd, out, timer, ms_full)
-    if args.cold:
-        cold_steps(torch, lambda: step(md), stream, max(5, args.steps), ms)
+    if args.cold or not args.quick:
+        rec["cold"] = cold_steps(torch, lambda: step(md), stream, 7, ms_med)
+    if not args.quick:
+        rec["dense_sdpa"] = dense_sdpa(torch, timer, qd, kd, vd, ms, ms_full)
     if args.ceiling or not args.quick:
-        ceil = gemm_ceiling(torch, timer)
-        ceil["headline_frac_of_best"] = round(rec["value"] / ceil["best_tflops"], 3)
-        ceil["full_mask_frac_of_best"] = round(rec["full_mask_tflops"] / ceil["best_tflops"], 3)
+        ceil = gemm_ceiling(bsa, torch, timer)
+        for key, ref in (("probe", ceil["mfma_probe_tflops"]), ("gemm", ceil["gemm_best_tflops"])):
+            ceil[f"headline_frac_of_{key}"] = round(rec["value"] / ref, 3)
+            ceil[f"full_mask_frac_of_{key}"] = round(rec["full_mask_tflops"] / ref, 3)
         rec["mfma_ceiling"] = ceil
     if not args.quick:
         rec["density_sweep"] = density_sweep(bsa, torch, w, qd, kd, vd, out, timer, ms_full)

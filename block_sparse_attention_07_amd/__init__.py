@@ -25,6 +25,7 @@ from .api import (  # noqa: F401
     mask_from_threshold_map,
     mask_resize,
     mask_words,
+    mfma_probe,
     permute_tokens,
     plan,
     sparse_attn,

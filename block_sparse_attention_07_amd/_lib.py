@@ -36,6 +36,7 @@ SIGNATURES = {
     "attn_fidelity": [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p, _p],
     "permute_tokens": [_p, _p, _i, _i, _i, _i, _i, _p, _p],
     "hilbert3d_order": [_i, _i, _i, _p],
+    "bsa_mfma_probe": [_i, _p, ctypes.c_longlong, _p, _p],
 }
 RESTYPES = {"sparse_attn_workspace_bytes": ctypes.c_size_t}
 EXPORTS = ["bsa_last_error", *SIGNATURES]

@@ -347,3 +347,18 @@ def hilbert3d_order(T: int, H: int, W: int) -> np.ndarray:
     rc = lib().hilbert3d_order(int(T), int(H), int(W), perm.ctypes.data_as(ctypes.c_void_p))
     check(rc, "hilbert3d_order")
     return perm
+
+
+@_on_device
+def mfma_probe(sink: torch.Tensor, iterations: int) -> float:
+    """Measurement aid beside the path: enqueue the register-only bf16 MFMA loop of
+    bsa_mfma_probe on the current stream of ``sink``'s device (fp32, at least
+    512 x compute units elements) and return the flops it performs; time the call
+    with events on that stream for the rate."""
+    _dev(sink)
+    _need(sink.dtype == torch.float32, "sink must be float32")
+    flops = ctypes.c_double(0.0)
+    rc = lib().bsa_mfma_probe(int(iterations), _ptr(sink), ctypes.c_longlong(sink.numel()),
+                              ctypes.byref(flops), _stream(sink))
+    check(rc, "bsa_mfma_probe")
+    return flops.value

@@ -37,6 +37,7 @@ SOURCES = [
     "resize.hip",
     "b128.hip",
     "noalloc.hip",
+    "probe.hip",
 ]
 EXTRA_FLAGS = {"topp.hip": ["-ffp-contract=off"]}
 

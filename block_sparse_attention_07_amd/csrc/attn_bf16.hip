@@ -6,7 +6,7 @@
 // computed densely, all other tiles are skipped without touching their K/V.
 //
 // gfx950 mapping (one workgroup of 4 waves per (head, query block); two query
-// blocks with identical mask rows share one workgroup, attn_pair_kernel below):
+// blocks with identical mask rows share one workgroup, pair_body below):
 //  * wave w owns query rows 32*(w&1) .. +31 and key half 32*(w>>1) .. +31 of every
 //    kept tile, so each wave keeps its own running max / sum and output
 //    accumulator; the two key halves are merged once at the end.
@@ -32,7 +32,7 @@
 //  * Softmax rescaling is lazy: the running max used for exponentials only moves
 //    when a tile's max exceeds it by more than 8 (a factor 256), which keeps every
 //    probability <= 256 and leaves the result exact up to rounding.
-//  * attn_pair_kernel: wave w owns the 32 query rows 32*(w&1) .. +31 of query block
+//  * pair_body: wave w owns the 32 query rows 32*(w&1) .. +31 of query block
 //    w>>1 and both key halves of every tile (no merge at the end).  Both kernels
 //    run two workgroups per CU, one wave of each per SIMD, and raise wave
 //    priority for their PV MFMAs so that one wave's MFMAs run while the other
@@ -182,7 +182,7 @@ __device__ __forceinline__ void single_row_body(
   const int g = lane >> 5;
 
   // Work entries: e in [0, H nb) is the single row e; pair entries (>= H nb,
-  // run by attn_pair_kernel) and empty slots (-1) are skipped.
+  // run by pair_body) and empty slots (-1) are skipped.
   //
   // With a work order the rows go out in slices.  The workgroups of a launch
   // are handed to the 8 XCDs in turn (workgroup i to XCD i mod 8); the XCDs
@@ -844,10 +844,10 @@ __device__ __forceinline__ void pair_body(
 }
 
 
-// The kernels: single rows, pair rows, and one launch holding the pair
-// workgroups followed by the last single-row slices (attn_mixed_kernel), so
+// The kernels: single rows, and one launch holding the pair workgroups
+// followed by the last single-row slices (attn_mixed_kernel), so
 // that single rows take the slots the pair launch's last, partial round leaves
-// free.  All three declare the same LDS objects.
+// free.  Both declare the same LDS objects.
 template <int D>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
@@ -861,20 +861,6 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
   __shared__ int nlist;
   single_row_body<D>(blockIdx.x, Q, K, VT, mask, order, stream_off, groups, n_heads, N, nb, W, c, O,
                      kst0, kst1, vts0, vts1, list, nlist);
-}
-
-template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_pair_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ VT,
-    const uint64_t* __restrict__ mask, const int32_t* __restrict__ order, int n_heads, int N,
-    int nb, int W, float c, u16* __restrict__ O) {
-  __shared__ __attribute__((aligned(16))) u16 kst0[BLK * D];
-  __shared__ __attribute__((aligned(16))) u16 kst1[BLK * D];
-  __shared__ __attribute__((aligned(16))) u16 vts0[D * BLK];
-  __shared__ __attribute__((aligned(16))) u16 vts1[D * BLK];
-  __shared__ __attribute__((aligned(16))) u16 list[LIST_CAP];
-  __shared__ int nlist;
-  pair_body<D>(blockIdx.x, Q, K, VT, mask, order, n_heads, N, nb, W, c, O, kst0, kst1, vts0, vts1, list, nlist);
 }
 
 // Workgroups [0, pair_wgs) are the pair launch (pair_wgs a multiple of 8; those

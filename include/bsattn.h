@@ -366,6 +366,24 @@ int permute_tokens(const void* x, const int32_t* perm, int n_heads, int seq_len,
  */
 int hilbert3d_order(int T, int H, int W, int32_t* perm_host);
 
+/*
+ * bsa_mfma_probe -- a measurement aid beside the attention path, not part of it.
+ * The roofline of the attention kernels is the bf16 MFMA rate; the data-sheet peak
+ * assumes a clock the chip does not hold under sustained MFMA load, so this probe
+ * measures the rate on the GPU itself: every wave of two 4-wave workgroups per CU
+ * runs `iterations` rounds of 16 v_mfma_f32_32x32x16_bf16 (four independent
+ * accumulator chains) on register operands, with no memory traffic.
+ *   sink        fp32 device buffer of sink_floats >= 512 * (compute units) floats; each
+ *               thread writes one sum there (keeps the work observable).
+ *   flops_host  host pointer; receives the flops the launch performs (time the call
+ *               with events on `stream` for the rate).
+ *   iterations  in [1, 1e7].
+ * Argument errors are returned before any device call, except the sink size, which
+ * is checked against the device's compute-unit count.
+ */
+int bsa_mfma_probe(int iterations, float* sink, long long sink_floats, double* flops_host,
+                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

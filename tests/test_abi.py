@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert sorted(names) == sorted(_lib.EXPORTS)
 
 
@@ -161,3 +161,17 @@ def test_b128_mask_alignment_and_expansion_argument_errors():
     assert L.mask_b128_to_b64(p(256), 1, 128, p(260), None) == 1      # uint64 output misaligned
     assert L.mask_b128_to_b64(p(256), 0, 128, p(256), None) == 1
     assert L.mask_b128_to_b64(p(256), 1, 0, p(256), None) == 1
+
+
+def test_mfma_probe_argument_errors_precede_any_device_call():
+    """The measurement probe rejects a bad iteration count, a null or misaligned
+    sink and a null flops pointer before any HIP call."""
+    L = _lib.lib()
+    f = ctypes.c_double(0.0)
+    sink = ctypes.c_void_p(1 << 20)
+    assert L.bsa_mfma_probe(0, sink, 1 << 20, ctypes.byref(f), None) == 1
+    assert L.bsa_mfma_probe(10_000_001, sink, 1 << 20, ctypes.byref(f), None) == 1
+    assert L.bsa_mfma_probe(10, None, 1 << 20, ctypes.byref(f), None) == 1
+    assert L.bsa_mfma_probe(10, ctypes.c_void_p((1 << 20) + 2), 1 << 20, ctypes.byref(f), None) == 1
+    assert L.bsa_mfma_probe(10, sink, 1 << 20, None, None) == 1
+    assert L.bsa_last_error().decode()
