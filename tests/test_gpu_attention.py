@@ -272,6 +272,36 @@ def test_every_row_once_across_xcd_groups(H, n, d):
     gu.assert_bf16_close(got2, ref, f"H={H} n={n} d={d} permuted")
 
 
+@pytest.mark.parametrize("H,n", [(6, 64 * 800 + 9), (8, 64 * 600 + 33)])
+def test_slices_beyond_the_pair_launch(H, n):
+    """More single-row slices than ride in the pair launch, with two XCD groups
+    (H = 6) and four (H = 8): pairs, the pair launch's trailing slices and the
+    later slice launches together write every row once (the output starts as NaN),
+    and sampled blocks, the ragged last one included, match the oracle."""
+    d = 64
+    nb = -(-n // B)
+    q, k, v = _rand_bf16(H, n, d, seed=H * 1000 + n % 1000)
+    rng = np.random.default_rng(H + n)
+    u = np.arange(nb)
+    keep = np.abs(u[:, None] - u[None, :]) <= 1
+    keep = np.broadcast_to(keep, (H, nb, nb)) | (rng.random((H, nb, nb)) < rng.uniform(0.02, 0.08, (H, 1, 1)))
+    for h in range(H):
+        for uu in range(0, nb - 1, 2):
+            if rng.random() < 0.1:
+                keep[h, uu + 1] = keep[h, uu]
+    keep[H - 1, 7] = False
+    bits = crm.pack_rows(keep)
+    out = torch.full((H, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    got = _run_bf16(q, k, v, bits, 0.125, out=out)
+    assert not np.isnan(got).any()
+    assert np.all(got[H - 1, 7 * B:8 * B] == 0.0)
+    blocks = [(0, 0), (H - 1, nb - 1), (H // 2, nb // 2)] + [(int(a), int(b)) for a, b in
+                                                            zip(rng.integers(0, H, 9), rng.integers(0, nb, 9))]
+    ref = sparse_attention(_f(q), _f(k), _f(v), bits, 0.125, blocks=blocks)
+    for (h, uu), r in zip(blocks, ref):
+        gu.assert_bf16_close(got[h, uu * B:uu * B + r.shape[0]], r, f"H={H} block ({h}, {uu})")
+
+
 def test_long_rows_past_the_planner_sort_limit():
     """More than 8192 query blocks per head: the planner keeps the rows in block
     order without pairs (its LDS sort covers 8192 rows), and the attention still
