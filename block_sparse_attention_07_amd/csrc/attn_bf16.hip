@@ -29,9 +29,14 @@
 //  * The row's kept-block list is decoded once per 2048 blocks by wave 0: one mask
 //    word per lane, popcount, and a ballot-based exclusive prefix (one ballot per
 //    bit of the count) give every lane its write offset into an LDS list.
-//  * Softmax rescaling is lazy: the running max used for exponentials only moves
-//    when a tile's max exceeds it by more than 8 (a factor 256), which keeps every
-//    probability <= 256 and leaves the result exact up to rounding.
+//  * Single rows first walk their tiles with the running max that the row's
+//    first tile sets, taking no max per tile: a NaN-safe test of each tile's
+//    probability sum (<= 2^20) goes into a sticky flag.  Only if some wave of the
+//    workgroup raised the flag does the workgroup walk the row again in the
+//    max-tracking form, whose rescaling is lazy: the running max used for
+//    exponentials moves when a tile's max exceeds it by more than 8 (a factor
+//    256).  Either walk keeps every probability within a range where the result
+//    is exact up to rounding.
 //  * pair_body: wave w owns the 32 query rows 32*(w&1) .. +31 of query block
 //    w>>1 and both key halves of every tile (no merge at the end).  Both kernels
 //    run two workgroups per CU, one wave of each per SIMD, and raise wave
@@ -237,6 +242,9 @@ __device__ __forceinline__ void single_row_body(
   // exp2(-inf) = 0 everywhere without a special case.
   float m_run = -1.0e30f;
   float l_part = 0.f;
+  // Set by the fast form when a tile's probabilities may have left the exact
+  // range (see run_row below).
+  bool over = false;
 
   // Both tiles travel by LDS DMA (global -> LDS without VGPRs).  One wave
   // instruction writes 1 KB: KR consecutive K rows, or 8 consecutive V^T rows.
@@ -296,45 +304,56 @@ __device__ __forceinline__ void single_row_body(
 #endif
   };
 
-  // One pipeline step for this wave: online softmax of S (tile vb, already in
-  // registers), the QK^T MFMAs of the next tile from K stage kbuf (returned),
-  // and O^T += V^T P^T from V stage vbuf.  The next tile's MFMAs do not depend on
-  // the softmax, so they are issued in the same straight-line block as the
-  // exponentials and interleaved with them (one MFMA, then a few VALU ops).
-  // s[i] is the logit of query row r32 for the key held by K row
-  // p0 + 8*(i/4) + 4*g + i%4, i.e. key 32kh + 16(i>>3) + 8g + (i&7).
-  auto step = [&](f32x16 s, int vb, int kbuf, int vbuf, bool may_be_ragged) {
-    if (may_be_ragged) {
-      const int hi = N - vb * BLK;   // tile positions >= hi lie past the sequence end
-      if (hi < BLK) {
-        // key of register i = lane base + a constant; compare the base with a
-        // scalar threshold per register
-        const int kbase = 32 * kh + 8 * g;
+  // Keys past the sequence end (only in the ragged last block) get -inf.
+  auto mask_ragged = [&](f32x16& s, int vb) {
+    const int hi = N - vb * BLK;   // tile positions >= hi lie past the sequence end
+    if (hi < BLK) {
+      // key of register i = lane base + a constant; compare the base with a
+      // scalar threshold per register
+      const int kbase = 32 * kh + 8 * g;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kbase >= hi - (16 * (i >> 3) + (i & 7))) s[i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (kbase >= hi - (16 * (i >> 3) + (i & 7))) s[i] = -INFINITY;
     }
-    // IEEE maximum (NaN-propagating) needs no input canonicalisation and maps to
-    // three-input v_maximum3_f32, so the 16-value max is 8 instructions.
+  };
+  // Max over this wave's 32 keys of the tile for the lane's query row.  IEEE
+  // maximum (NaN-propagating) needs no input canonicalisation and maps to
+  // three-input v_maximum3_f32, so the 16 lane-local values take 8 instructions;
+  // lanes l and l^32 hold the two 16-key halves of the same query row.
+  auto row_max = [&](const f32x16& s) {
     float mx = __builtin_elementwise_maximum(s[0], s[1]);
 #pragma unroll
     for (int i = 2; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s[i]);
-    {
-      // lanes l and l^32 hold the two 16-key halves of the same query row
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt = mx * c;       // -inf when every key of this half is masked
-    if (__any(mt > m_run + RESCALE_SLACK)) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      l_part *= alpha;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+
+  // One pipeline step for this wave: online softmax of S (tile vb, already in
+  // registers), the QK^T MFMAs of the next tile from K stage kbuf (returned),
+  // and O^T += V^T P^T from V stage vbuf.  The fast form (SAFE false) keeps the
+  // running max the row's first tile set and only records whether a tile's
+  // probabilities could have left the range the result is exact in; the safe
+  // form checks each tile's max first and rescales lazily.  The next tile's
+  // MFMAs do not depend on the softmax, so they are issued in the same
+  // straight-line block as the exponentials and interleaved with them (one
+  // MFMA, then a few VALU ops).
+  // s[i] is the logit of query row r32 for the key held by K row
+  // p0 + 8*(i/4) + 4*g + i%4, i.e. key 32kh + 16(i>>3) + 8g + (i&7).
+  auto step = [&](f32x16 s, int vb, int kbuf, int vbuf, bool may_be_ragged, auto safe) {
+    constexpr bool SAFE = decltype(safe)::value;
+    if (may_be_ragged) mask_ragged(s, vb);
+    if constexpr (SAFE) {
+      const float mt = row_max(s) * c;   // -inf when every key of this half is masked
+      if (__any(mt > m_run + RESCALE_SLACK)) {
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_part *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m_run = mn;
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        m_run = mn;
+      }
     }
     // --- straight-line block: next tile's QK^T interleaved with this tile's exp2
     f32x16 sn;
@@ -388,7 +407,9 @@ __device__ __forceinline__ void single_row_body(
         ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb0[2 * j], pb0[2 * j + 1]}, one, ls0, false);
         ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb1[2 * j], pb1[2 * j + 1]}, one, ls1, false);
       }
-      l_part += ls0 + ls1;
+      const float ls = ls0 + ls1;
+      if constexpr (!SAFE) over = over || !(ls <= SUM_LIMIT);   // also catches inf and NaN
+      l_part += ls;
     }
     __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
 #pragma unroll
@@ -404,13 +425,10 @@ __device__ __forceinline__ void single_row_body(
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = 32 * db + r32;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int s0 = 0; s0 < 2; ++s0) {
+      for (int s0 = 0; s0 < 2; ++s0)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][s0], s0 ? pb1 : pb0, o[db], 0, 0, 0);
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     return sn;
@@ -433,73 +451,106 @@ __device__ __forceinline__ void single_row_body(
   const uint64_t lastmask = tail_bits ? ((1ull << tail_bits) - 1ull) : ~0ull;
   const uint64_t lanes_below = (1ull << lane) - 1ull;
 
-  for (int w0 = 0; w0 < W; w0 += CHUNK_WORDS) {
-    __syncthreads();   // every wave is done with the previous chunk's list
-    if (wave == 0) {
-      const int wi = w0 + lane;
-      uint64_t word = 0;
-      if (lane < CHUNK_WORDS && wi < W) {
-        word = mrow[wi];
-        if (wi == W - 1) word &= lastmask;
-      }
-      const int cnt = __popcll(word);
-      int pre = 0, tot = 0;
+  // The row's tile walk.  The fast form runs first; if any lane of any wave
+  // saw a tile whose bf16 probability sum exceeds SUM_LIMIT (or is not
+  // finite), its output could have lost accuracy or overflowed, and the whole
+  // workgroup walks the row again in the safe form, which tracks the max tile by
+  // tile.  On inputs whose logits stay within 20 (exp2 domain) of the first
+  // tile's max the safe form never runs.
+  int first_w0 = -1;
+  auto run_row = [&](auto safe) {
+    constexpr bool SAFE = decltype(safe)::value;
+    for (int w0 = 0; w0 < W; w0 += CHUNK_WORDS) {
+      __syncthreads();   // every wave is done with the previous chunk's list
+      if (wave == 0) {
+        const int wi = w0 + lane;
+        uint64_t word = 0;
+        if (lane < CHUNK_WORDS && wi < W) {
+          word = mrow[wi];
+          if (wi == W - 1) word &= lastmask;
+        }
+        const int cnt = __popcll(word);
+        int pre = 0, tot = 0;
 #pragma unroll
-      for (int b = 0; b < 7; ++b) {
-        const uint64_t bal = __ballot((cnt >> b) & 1);
-        pre += __popcll(bal & lanes_below) << b;
-        tot += __popcll(bal) << b;
+        for (int b = 0; b < 7; ++b) {
+          const uint64_t bal = __ballot((cnt >> b) & 1);
+          pre += __popcll(bal & lanes_below) << b;
+          tot += __popcll(bal) << b;
+        }
+        const int base = 64 * wi;
+        while (word) {
+          list[pre++] = (u16)(base + __ffsll((unsigned long long)word) - 1);
+          word &= word - 1ull;
+        }
+        if (lane == 0) nlist = tot;
       }
-      const int base = 64 * wi;
-      while (word) {
-        list[pre++] = (u16)(base + __ffsll((unsigned long long)word) - 1);
-        word &= word - 1ull;
-      }
-      if (lane == 0) nlist = tot;
-    }
-    __syncthreads();
-    const int n = nlist;
-    if (n == 0) continue;
-    // Software pipeline with K one tile ahead of V.  At the top of step t the K
-    // stage (t+1)&1 holds K(t+1), the V stage t&1 holds V(t) and S(t) is in
-    // registers; the K stage t&1 and the V stage (t+1)&1 were last read in step
-    // t-1.  Step t starts the DMA of K(t+2) and V(t+1) into those two stages,
-    // runs the QK^T MFMAs of tile t+1 next to the softmax of tile t
-    // (independent work the scheduler can interleave), then PV of tile t; the
-    // barrier at its end (whose fence waits for the wave's DMA) publishes both
-    // stages.  Past the end of the list the last tile is used again (loads stay
-    // unconditional; the extra S is discarded).
-    // Lane j of lv holds list entry t0 + j (clamped to the last entry), so a
-    // step takes its tile indices with v_readlane instead of an LDS round trip
-    // on its critical path; the window moves once every 60 steps or so.
-    int t0 = 0;
-    int lv = list[min(lane, n - 1)];
-    auto tile = [&](int t) { return __builtin_amdgcn_readlane(lv, t - t0); };
-    // only the last block of the sequence can be ragged, and it is always the
-    // last entry of an ascending list
-    kdma(tile(0), 0);
-    vdma(tile(0), 0);
-    __syncthreads();
-    kdma(tile(1), 1);
-    f32x16 s_cur = qk(0);
-    __syncthreads();
-    // The loop is unrolled by two so each step's stage indices are constants and
-    // every LDS address is a per-lane base plus an instruction offset.
-    auto body = [&](int t, auto parity) {
-      constexpr int P = decltype(parity)::value;   // t & 1
-      kdma(tile(t + 2), P);
-      vdma(tile(t + 1), P ^ 1);
-      s_cur = step(s_cur, tile(t), P ^ 1, P, t == n - 1);
       __syncthreads();
-    };
-    for (int t = 0; t < n; t += 2) {
-      if (t + 3 - t0 > 63) {      // the two steps below read entries up to t + 3
-        t0 = t;
-        lv = list[min(t0 + lane, n - 1)];
+      const int n = nlist;
+      if (n == 0) continue;
+      if (first_w0 < 0) first_w0 = w0;
+      // Software pipeline with K one tile ahead of V.  At the top of step t the K
+      // stage (t+1)&1 holds K(t+1), the V stage t&1 holds V(t) and S(t) is in
+      // registers; the K stage t&1 and the V stage (t+1)&1 were last read in step
+      // t-1.  Step t starts the DMA of K(t+2) and V(t+1) into those two stages,
+      // runs the QK^T MFMAs of tile t+1 next to the softmax of tile t
+      // (independent work the scheduler can interleave), then PV of tile t; the
+      // barrier at its end (whose fence waits for the wave's DMA) publishes both
+      // stages.  Past the end of the list the last tile is used again (loads stay
+      // unconditional; the extra S is discarded).
+      // Lane j of lv holds list entry t0 + j (clamped to the last entry), so a
+      // step takes its tile indices with v_readlane instead of an LDS round trip
+      // on its critical path; the window moves once every 60 steps or so.
+      int t0 = 0;
+      int lv = list[min(lane, n - 1)];
+      auto tile = [&](int t) { return __builtin_amdgcn_readlane(lv, t - t0); };
+      // only the last block of the sequence can be ragged, and it is always the
+      // last entry of an ascending list
+      kdma(tile(0), 0);
+      vdma(tile(0), 0);
+      __syncthreads();
+      kdma(tile(1), 1);
+      f32x16 s_cur = qk(0);
+      if (!SAFE && w0 == first_w0) {
+        // the fast form takes the running max from the row's first tile
+        mask_ragged(s_cur, tile(0));
+        m_run = fmaxf(row_max(s_cur) * c, -1.0e30f);
       }
-      body(t, std::integral_constant<int, 0>{});
-      if (t + 1 < n) body(t + 1, std::integral_constant<int, 1>{});
+      __syncthreads();
+      // The loop is unrolled by two so each step's stage indices are constants and
+      // every LDS address is a per-lane base plus an instruction offset.
+      auto body = [&](int t, auto parity) {
+        constexpr int P = decltype(parity)::value;   // t & 1
+        kdma(tile(t + 2), P);
+        vdma(tile(t + 1), P ^ 1);
+        s_cur = step(s_cur, tile(t), P ^ 1, P, t == n - 1, safe);
+        __syncthreads();
+      };
+      for (int t = 0; t < n; t += 2) {
+        if (t + 3 - t0 > 63) {      // the two steps below read entries up to t + 3
+          t0 = t;
+          lv = list[min(t0 + lane, n - 1)];
+        }
+        body(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n) body(t + 1, std::integral_constant<int, 1>{});
+      }
     }
+  };
+  run_row(std::false_type{});
+  // Workgroup-wide vote on the fast form's flag (nlist is free here: every wave
+  // is past its last read of it).
+  __syncthreads();
+  if (tid == 0) nlist = 0;
+  __syncthreads();
+  if (__any(over) && lane == 0) nlist = 1;
+  __syncthreads();
+  if (nlist) {
+    m_run = -1.0e30f;
+    l_part = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    run_row(std::true_type{});
   }
 
   // Merge the two key halves of each query-row half and write the output.

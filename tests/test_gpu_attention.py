@@ -137,6 +137,33 @@ def test_bf16_rescale_stress_growing_keys():
     gu.assert_bf16_close(_run_bf16(q, k, v, bits, scale), sparse_attention(_f(q), _f(k), _f(v), bits, scale), "rescale")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_rescale_stress_single_rows(d):
+    """Growing keys on distinct random rows, all run as single rows (an identity
+    work order pairs nothing): logits in later tiles exceed the first tile's max by
+    far more than the fast tile walk accepts, so those rows go through the
+    max-tracking walk; flat rows beside them stay on the fast one."""
+    n = 64 * 12 + 5
+    nb = -(-n // B)
+    rng = np.random.default_rng(21)
+    growth = (1.0 + 0.6 * (np.arange(n) // B))[None, :, None]
+    q = workloads.bf16_bits(rng.standard_normal((2, n, d)).astype(np.float32))
+    kf = rng.standard_normal((2, n, d))
+    kf[0] *= growth[0]                       # head 0 grows, head 1 stays flat
+    k = workloads.bf16_bits(kf.astype(np.float32))
+    v = workloads.bf16_bits(rng.standard_normal((2, n, d)).astype(np.float32))
+    keep = rng.random((2, nb, nb)) < 0.5
+    keep[:, np.arange(nb), np.arange(nb)] = True
+    keep[:, :, 0] = True                     # every row starts at the smallest keys
+    bits = crm.pack_rows(keep)
+    scale = 1.0 / np.sqrt(d)
+    ref = sparse_attention(_f(q), _f(k), _f(v), bits, scale)
+    order = torch.arange(2 * nb, dtype=torch.int32, device="cuda")
+    got = _run_bf16(q, k, v, bits, scale, work_order=order)
+    gu.assert_bf16_close(got, ref, "rescale single rows")
+    gu.assert_bf16_close(_run_bf16(q, k, v, bits, scale), ref, "rescale planned")
+
+
 def test_bf16_zero_query_probe_pins_the_kept_set():
     """q = 0: each output is the token-weighted mean of the kept blocks' values;
     V carries each key's block id in binary, so a dropped or extra block shows up
