@@ -216,6 +216,11 @@ __device__ __forceinline__ void single_row_body(
   const u16* VTh = VT + (size_t)h * D * npad;
   const uint64_t* mrow = mask + ((size_t)h * nb + u) * W;
 
+  // The first chunk's mask words are requested ahead of Q, so the two loads'
+  // latencies overlap (wave 0 decodes the chunks; see run_row).
+  uint64_t word0 = 0;
+  if (wave == 0 && lane < CHUNK_WORDS && lane < W) word0 = mrow[lane];
+
   // Q^T fragments (B operand): lane holds Q[row][16ks + 8g .. +7] of its query row.
   bf16x8 qf[NKS];
   {
@@ -466,7 +471,7 @@ __device__ __forceinline__ void single_row_body(
         const int wi = w0 + lane;
         uint64_t word = 0;
         if (lane < CHUNK_WORDS && wi < W) {
-          word = mrow[wi];
+          word = w0 == 0 ? word0 : mrow[wi];
           if (wi == W - 1) word &= lastmask;
         }
         const int cnt = __popcll(word);
@@ -504,11 +509,12 @@ __device__ __forceinline__ void single_row_body(
       int lv = list[min(lane, n - 1)];
       auto tile = [&](int t) { return __builtin_amdgcn_readlane(lv, t - t0); };
       // only the last block of the sequence can be ragged, and it is always the
-      // last entry of an ascending list
+      // last entry of an ascending list.  The first two K tiles and the first V
+      // tile go out together and land behind one barrier.
       kdma(tile(0), 0);
       vdma(tile(0), 0);
-      __syncthreads();
       kdma(tile(1), 1);
+      __syncthreads();
       f32x16 s_cur = qk(0);
       if (!SAFE && w0 == first_w0) {
         // the fast form takes the running max from the row's first tile
@@ -853,8 +859,8 @@ __device__ __forceinline__ void pair_body(
     auto tile = [&](int t) { return __builtin_amdgcn_readlane(lv, t - t0); };
     kdma(tile(0), 0);
     vdma(tile(0), 0);
-    __syncthreads();
     kdma(tile(1), 1);
+    __syncthreads();
     f32x16 s0 = qk(0, 0), s1 = qk(0, 1);
     __syncthreads();
     auto body = [&](int t, auto parity) {
