@@ -805,16 +805,28 @@ __device__ __forceinline__ void pair_body(
       }
     }
     l_part += lh[0] + lh[1];
+    // V^T operand of PV MFMA (k-slot j: keys 16 j .. 16 j + 15, column block db).
+    // Key half 0's operands are read ahead of the raised-priority PV block, in
+    // the registers the K operands held, so its first MFMAs do not each wait for
+    // an LDS round trip; the wave has no registers left to read half 1's ahead too.
+    auto vread = [&](int j, int db) {
+      const int d = 32 * db + r32;
+      const int chunk = (2 * j + g) ^ v_swz(d);
+      return *reinterpret_cast<const bf16x8*>(vstage(vbuf) + d * BLK + 8 * chunk);
+    };
+    constexpr int PRE = 2 * NDB;
+    bf16x8 vpre[PRE];
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) vpre[i] = vread(i / NDB, i % NDB);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {           // k-slot j: keys 16 j .. 16 j + 15
+    for (int j = 0; j < 4; ++j) {
       const int kh = j >> 1, s0i = j & 1;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + r32;
-        const int chunk = (4 * kh + 2 * s0i + g) ^ v_swz(d);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vstage(vbuf) + d * BLK + 8 * chunk);
+        const int i = j * NDB + db;
+        const bf16x8 a = i < PRE ? vpre[i < PRE ? i : 0] : vread(j, db);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][s0i], o[db], 0, 0, 0);
       }
     }
