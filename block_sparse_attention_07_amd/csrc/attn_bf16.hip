@@ -1015,9 +1015,12 @@ int launch_generations(const u16* Q, const u16* K, const u16* V, const uint64_t*
   // short, and hold rows at all unless every row of those heads is paired (the
   // heads whose rows are all paired are the full ones, which rank first by total
   // work, so their empty single-row slots are the first slices).  The other
-  // slices follow one launch each, heaviest first.
-  constexpr int MIX = 8;
+  // slices follow one launch each, heaviest first.  A layer of at most 16
+  // slices sends them all with the pairs: its heads are small and its rows
+  // short, so a launch boundary per slice costs more than the common start
+  // gains (Wan2.1-1.3B 480p: 1.78 -> 1.74 ms).
   const int slices = groups == 1 ? (total + gen - 1) / gen : (len + per - 1) / per;
+  const int MIX = slices <= 16 ? slices : 8;
   int last = slices;                            // slices [last, slices) ride with the pairs
   if (order && nb >= 2) {
     const int pair_wgs = (n_heads * (nb / 2) + 7) & ~7;

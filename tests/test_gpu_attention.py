@@ -268,6 +268,35 @@ def test_rows_beyond_one_decode_chunk():
         gu.assert_bf16_close(got[h, u * B:u * B + r.shape[0]], r, f"block {u}")
 
 
+def test_decode_chunks_first_empty_and_growing_keys():
+    """Rows spanning two 2048-block decode chunks, all run as single rows.  Some
+    rows keep nothing in the first chunk, so the running max comes from the
+    second chunk's first tile.  Others keep nothing in the second chunk.  In
+    head 1, the keys of the second chunk are scaled up so that its logits pass
+    the first chunk's max by far more than the fast walk accepts, and those rows
+    are walked again, across both chunks, with the max tracked tile by tile."""
+    n, d = 64 * 2100 + 10, 64
+    nb = -(-n // B)
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((2, n, d)).astype(np.float32) for _ in range(3))
+    k[1, 2048 * B:] *= 6.0
+    q, k, v = (workloads.bf16_bits(x) for x in (q, k, v))
+    keep = rng.random((2, nb, nb)) < 0.02
+    keep[:, :, 10] = True
+    keep[:, :, 2060] = True
+    keep[:, 3, :2048] = False                        # first chunk empty
+    keep[:, 4, 2048:] = False                        # second chunk empty
+    keep[:, 5] = False                               # empty row
+    keep[:, 5, nb - 1] = True                        # ... but for the ragged last block
+    bits = crm.pack_rows(keep)
+    order = torch.arange(2 * nb, dtype=torch.int32, device="cuda")
+    got = _run_bf16(q, k, v, bits, 0.125, work_order=order)
+    blocks = [(h, u) for h in (0, 1) for u in (0, 3, 4, 5, 2047, nb - 1)]
+    ref = sparse_attention(_f(q), _f(k), _f(v), bits, 0.125, blocks=blocks)
+    for (h, u), r in zip(blocks, ref):
+        gu.assert_bf16_close(got[h, u * B:u * B + r.shape[0]], r, f"head {h} block {u}")
+
+
 @pytest.mark.parametrize("H,n,d", [(8, 64 * 70 + 17, 128), (12, 64 * 45, 64), (6, 64 * 90 + 3, 128),
                                    (5, 64 * 110, 64)])
 def test_every_row_once_across_xcd_groups(H, n, d):
