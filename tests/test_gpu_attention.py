@@ -328,12 +328,15 @@ def test_every_row_once_across_xcd_groups(H, n, d):
     gu.assert_bf16_close(got2, ref, f"H={H} n={n} d={d} permuted")
 
 
-@pytest.mark.parametrize("H,n", [(6, 64 * 800 + 9), (8, 64 * 600 + 33)])
+@pytest.mark.parametrize("H,n", [(6, 64 * 800 + 9), (8, 64 * 600 + 33), (6, 64 * 1400 + 9),
+                                 (8, 64 * 1100 + 33)])
 def test_slices_beyond_the_pair_launch(H, n):
-    """More single-row slices than ride in the pair launch, with two XCD groups
-    (H = 6) and four (H = 8): pairs, the pair launch's trailing slices and the
-    later slice launches together write every row once (the output starts as NaN),
-    and sampled blocks, the ragged last one included, match the oracle."""
+    """Single-row slices with two XCD groups (H = 6) and four (H = 8).  At the
+    smaller lengths (10 slices) every slice rides in the pair launch.  At the
+    larger ones (more than 16 slices) the last eight do, and the others go out
+    one launch each.  Pairs, the pair launch's slices and the later slice
+    launches together write every row once (the output starts as NaN), and
+    sampled blocks, the ragged last one included, match the oracle."""
     d = 64
     nb = -(-n // B)
     q, k, v = _rand_bf16(H, n, d, seed=H * 1000 + n % 1000)
