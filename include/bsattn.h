@@ -176,7 +176,8 @@ int sparse_attn_plan(const uint64_t* mask_bits, int n_heads, int seq_len, int bl
  * workgroups each (compute units x resident workgroups per unit), so that the rows of each
  * slice start together.  The pair entries share one launch with the last eight slices
  * (pair workgroups first, the slices behind them: the lightest rows, which fill the
- * pairs' last round); the other slices follow as consecutive kernel launches.  The
+ * pairs' last round), or with every slice when there are at most 16; the other slices
+ * follow as consecutive kernel launches.  The
  * XCDs are split into G groups (G = 4 when n_heads is a multiple of 4, else 2 when it
  * is even, else 1): group g walks the segments g, g + G, g + 2G, ... back to back, and
  * each launch takes the next device-full / G slots of every group's walk, so the K/V
