@@ -48,7 +48,8 @@
 //    different heads (see the row decode in single_row_body).  The pair
 //    workgroups and the last few single-row slices (the lightest heads' rows)
 //    share one launch (attn_mixed_kernel), so single rows fill the slots the
-//    pairs' last, partial round leaves idle.
+//    pairs' last, partial round leaves idle; a layer of at most 16 slices sends
+//    all of them with the pairs.
 #include <cmath>
 #include <type_traits>
 
